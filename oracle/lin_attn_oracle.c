@@ -1,0 +1,241 @@
+/*
+ * lin_attn_oracle.c -- slow, plain fp64 CPU oracle for causal linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this file.  Its only users are the tests under tests/, the
+ * smoke check in __graft_entry__.smoke() and the CPU baseline leg of bench.py.
+ * It shares no code, header, table or constant with the HIP library.
+ *
+ * What it computes (the plain definition, nothing reordered or blocked):
+ *
+ *   "MiniMax-M1で理解する：大規模言語モデルのコンテキスト長限界を突破する
+ *   革新的アーキテクチャ" (zenn.dev/liushuzhi), section
+ *   "線形アテンションの数学的基礎": linear attention with a feature map phi,
+ *   computed through its recurrent form
+ *        S_t = S_{t-1} + phi(k_t) v_t^T,       o_t = phi(q_t) S_t ,
+ *   with a state S in R^{D x d} whose update costs O(Dd) per token.
+ *
+ *   Readings taken where the page is silent: phi is the identity (D = d), no
+ *   decay, no normaliser, no 1/sqrt(d) scale; o_t reads the state AFTER the
+ *   token's own k_t v_t^T was added (so the causal mask includes the
+ *   diagonal); S[i][j] has row i = key feature, column j = value feature.
+ *
+ * The tiled ("Lightning") form is an exact re-association of the same sums
+ * ("Почему M2 в итоге стала моделью с полным вниманием?" (ai.flicky.cc),
+ * section 1, glossary entry "Lightning Attention": a masked matrix inside a
+ * block and a K^T V state between blocks), so this token-by-token loop is
+ * the oracle for every block size.
+ *
+ * Inputs arrive as float32 arrays: fp32 and bf16 values are both exactly
+ * representable in fp32, and every value is widened to double exactly before
+ * use.  All arithmetic is IEEE double; build without -ffast-math and with
+ * -ffp-contract=off.
+ *
+ * The bf16-stored-state variant (lao_decode_bf16_state) models a state that
+ * is kept in bfloat16 between steps -- the low-precision storage hazard that
+ * "ノーフリーランチ：MiniMax M2が高効率アテンション機構を解体"
+ * (winzheng.jp), section "推論システム統合の課題", and section 4 of the
+ * ai.flicky.cc digest describe: the state is widened to double, updated,
+ * read out, then rounded to bf16 (round to nearest, ties to even) once.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { LAO_OK = 0, LAO_EINVAL = -1, LAO_ENOMEM = -2 };
+
+/* ---------------------------------------------------------------------- */
+/* One (batch, head) recurrence.                                           */
+/* q, k, v : [N][d] float32 ; o : [N][d] double (out) ;                    */
+/* S : [d][d] double (in: S_0, out: S_N).                                  */
+/* ---------------------------------------------------------------------- */
+static void recurrence_one_head(const float *q, const float *k,
+                                const float *v, double *o, double *S,
+                                int64_t N, int64_t d) {
+  for (int64_t t = 0; t < N; ++t) {
+    const float *qt = q + t * d;
+    const float *kt = k + t * d;
+    const float *vt = v + t * d;
+    double *ot = o + t * d;
+    /* S_t = S_{t-1} + k_t v_t^T */
+    for (int64_t i = 0; i < d; ++i) {
+      const double ki = (double)kt[i];
+      double *Si = S + i * d;
+      for (int64_t j = 0; j < d; ++j) Si[j] += ki * (double)vt[j];
+    }
+    /* o_t[j] = sum_i q_t[i] S_t[i][j] */
+    for (int64_t j = 0; j < d; ++j) ot[j] = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      const double qi = (double)qt[i];
+      const double *Si = S + i * d;
+      for (int64_t j = 0; j < d; ++j) ot[j] += qi * Si[j];
+    }
+  }
+}
+
+/* Round a double to the nearest bfloat16, ties to even; returns the bf16 bit
+ * pattern.  Written from the format's definition: 1 sign bit, 8 exponent
+ * bits (same as binary32), 7 stored fraction bits.  The value is scaled so
+ * that the bf16 grid of its binade becomes the integers, rounded once with
+ * rint() (nearest, ties to even, in the default rounding mode), and scaled
+ * back; there is no intermediate rounding to binary32. */
+static uint16_t double_to_bf16_rne(double x) {
+  if (isnan(x)) return (uint16_t)0x7fc0;
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  /* bf16 largest finite = (2 - 2^-7) * 2^127; halfway to 2^128 rounds up */
+  const double max_finite = ldexp(2.0 - ldexp(1.0, -7), 127);
+  const double overflow_edge = ldexp(2.0 - ldexp(1.0, -8), 127);
+  if (a >= overflow_edge) return (uint16_t)(sign | 0x7f80); /* inf */
+  int e;
+  frexp(a, &e);           /* a = m * 2^e, m in [0.5, 1) */
+  int unb = e - 1;        /* a in [2^unb, 2^(unb+1)) */
+  if (unb < -126) unb = -126; /* subnormal range uses the smallest exponent */
+  /* spacing of bf16 values in this binade: 2^(unb-7) */
+  double scaled = ldexp(a, 7 - unb); /* in [128, 256) for normals */
+  double r = rint(scaled);           /* nearest, ties to even */
+  double y = ldexp(r, unb - 7);
+  if (y > max_finite) return (uint16_t)(sign | 0x7f80);
+  /* encode y exactly */
+  float f = (float)y; /* exact: y has <= 8 significant bits */
+  uint32_t bits;
+  memcpy(&bits, &f, sizeof bits);
+  return (uint16_t)(sign | ((bits >> 16) & 0x7fff));
+}
+
+static double bf16_to_double(uint16_t b) {
+  uint32_t bits = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* One decode token step per head with the state stored as bf16. */
+static void decode_bf16_state_one_head(const float *q, const float *k,
+                                       const float *v, double *o,
+                                       uint16_t *Sb, double *work,
+                                       int64_t d) {
+  for (int64_t i = 0; i < d; ++i)
+    for (int64_t j = 0; j < d; ++j) work[i * d + j] = bf16_to_double(Sb[i * d + j]);
+  recurrence_one_head(q, k, v, o, work, 1, d);
+  for (int64_t i = 0; i < d; ++i)
+    for (int64_t j = 0; j < d; ++j) Sb[i * d + j] = double_to_bf16_rne(work[i * d + j]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Thread fan-out over heads.                                              */
+/* ---------------------------------------------------------------------- */
+typedef struct {
+  const float *q, *k, *v;
+  double *o;
+  double *S;
+  uint16_t *Sb;
+  int64_t nheads, N, d;
+  int64_t next_head; /* guarded by mu */
+  pthread_mutex_t mu;
+  int bf16_state;
+} job_t;
+
+static void *worker(void *arg) {
+  job_t *jb = (job_t *)arg;
+  double *work = NULL;
+  if (jb->bf16_state) {
+    work = (double *)malloc(sizeof(double) * (size_t)(jb->d * jb->d));
+    if (!work) return (void *)1;
+  }
+  for (;;) {
+    pthread_mutex_lock(&jb->mu);
+    int64_t h = jb->next_head++;
+    pthread_mutex_unlock(&jb->mu);
+    if (h >= jb->nheads) break;
+    const int64_t td = jb->N * jb->d;
+    if (jb->bf16_state)
+      decode_bf16_state_one_head(jb->q + h * td, jb->k + h * td, jb->v + h * td,
+                                 jb->o + h * td, jb->Sb + h * jb->d * jb->d, work,
+                                 jb->d);
+    else
+      recurrence_one_head(jb->q + h * td, jb->k + h * td, jb->v + h * td,
+                          jb->o + h * td, jb->S + h * jb->d * jb->d, jb->N, jb->d);
+  }
+  free(work);
+  return NULL;
+}
+
+static int run_job(job_t *jb, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > jb->nheads) nthreads = (int)(jb->nheads > 0 ? jb->nheads : 1);
+  pthread_mutex_init(&jb->mu, NULL);
+  jb->next_head = 0;
+  int rc = LAO_OK;
+  if (nthreads == 1) {
+    if (worker(jb) != NULL) rc = LAO_ENOMEM;
+  } else {
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!th) {
+      pthread_mutex_destroy(&jb->mu);
+      return LAO_ENOMEM;
+    }
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+      if (pthread_create(&th[i], NULL, worker, jb) != 0) break;
+      ++started;
+    }
+    if (started == 0) { /* no threads at all: run inline */
+      if (worker(jb) != NULL) rc = LAO_ENOMEM;
+    }
+    for (int i = 0; i < started; ++i) {
+      void *ret = NULL;
+      pthread_join(th[i], &ret);
+      if (ret != NULL) rc = LAO_ENOMEM;
+    }
+    free(th);
+  }
+  pthread_mutex_destroy(&jb->mu);
+  return rc;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Exported entry points (called from oracle/oracle.py through ctypes).    */
+/* ---------------------------------------------------------------------- */
+
+/* Token-by-token recurrence over `nheads` independent (batch, head) pairs.
+ * q, k, v : [nheads][N][d] float32 ; o : [nheads][N][d] double (out) ;
+ * state : [nheads][d][d] double, in: S_0, out: S_N.
+ * A decode step is the same call with N = 1. */
+int lao_recurrence(const float *q, const float *k, const float *v, double *o,
+                   double *state, int64_t nheads, int64_t N, int64_t d,
+                   int nthreads) {
+  if (nheads < 0 || N < 0 || d <= 0) return LAO_EINVAL;
+  if (nheads == 0 || N == 0) return LAO_OK;
+  if (!q || !k || !v || !o || !state) return LAO_EINVAL;
+  job_t jb;
+  memset(&jb, 0, sizeof jb);
+  jb.q = q; jb.k = k; jb.v = v; jb.o = o; jb.S = state;
+  jb.nheads = nheads; jb.N = N; jb.d = d; jb.bf16_state = 0;
+  return run_job(&jb, nthreads);
+}
+
+/* One decode step per head with a bf16-stored state (in place).
+ * q, k, v : [nheads][d] float32 ; o : [nheads][d] double (out) ;
+ * state_bf16 : [nheads][d][d] bf16 bit patterns, in and out. */
+int lao_decode_bf16_state(const float *q, const float *k, const float *v,
+                          double *o, uint16_t *state_bf16, int64_t nheads,
+                          int64_t d, int nthreads) {
+  if (nheads < 0 || d <= 0) return LAO_EINVAL;
+  if (nheads == 0) return LAO_OK;
+  if (!q || !k || !v || !o || !state_bf16) return LAO_EINVAL;
+  job_t jb;
+  memset(&jb, 0, sizeof jb);
+  jb.q = q; jb.k = k; jb.v = v; jb.o = o; jb.Sb = state_bf16;
+  jb.nheads = nheads; jb.N = 1; jb.d = d; jb.bf16_state = 1;
+  return run_job(&jb, nthreads);
+}
+
+/* Exposed so the tests can pin the rounding against an independent library
+ * conversion. */
+void lao_round_bf16(const double *x, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = double_to_bf16_rne(x[i]);
+}

@@ -1,0 +1,201 @@
+"""fp64 CPU oracle for causal linear attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  It shares no code with the HIP library
+(``linear_attention_lightning_amd``) and imports nothing from it.
+
+The arithmetic lives in ``lin_attn_oracle.c`` (plain C, IEEE double, no
+blocking or reordering): the token-by-token recurrence
+
+    S_t = S_{t-1} + k_t v_t^T ,   o_t = q_t^T S_t
+
+of "MiniMax-M1で理解する：大規模言語モデルのコンテキスト長限界を突破する革新的
+アーキテクチャ" (zenn.dev/liushuzhi), section "線形アテンションの数学的基礎",
+recurrence equations, with phi = identity.  This module only compiles that
+file, marshals numpy arrays into it and back, and picks a thread count.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lin_attn_oracle.c")
+_LIB = os.path.join(_HERE, "liblin_attn_oracle.so")
+
+# Portable x86-64 baseline with AVX2 (runs on this container's Xeon and on
+# EPYC hosts); no -ffast-math, no FMA contraction, so every product and sum is
+# a separately rounded IEEE double operation.
+_CFLAGS = ["-O3", "-std=c11", "-march=x86-64-v3", "-ffp-contract=off",
+           "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library in place and return its path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.lao_recurrence.argtypes = [p, p, p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.lao_recurrence.restype = ctypes.c_int
+    lib.lao_decode_bf16_state.argtypes = [p, p, p, p, p, i64, i64, ctypes.c_int]
+    lib.lao_decode_bf16_state.restype = ctypes.c_int
+    lib.lao_round_bf16.argtypes = [p, p, i64]
+    lib.lao_round_bf16.restype = None
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            _lib = _bind(_LIB)
+    return _lib
+
+
+def compile_variant(src_text: str, out_path: str):
+    """Compile C source text with the oracle's flags and bind it like the
+    oracle.  Used by the tests to plant a mistake in a copy of the oracle and
+    show that the pins catch it; returns an object whose ``recurrence``
+    behaves like :func:`recurrence`."""
+    src_path = out_path + ".c"
+    with open(src_path, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", *_CFLAGS, "-o", out_path, src_path, "-lm"], check=True)
+    lib = _bind(out_path)
+
+    class _Variant:
+        @staticmethod
+        def recurrence(q, k, v, S0=None, nthreads=None):
+            return recurrence(q, k, v, S0, nthreads, _lib_obj=lib)
+
+    return _Variant()
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def default_threads() -> int:
+    """Host threads to use: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when that is set (it bounds the process's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _f32(x) -> np.ndarray:
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    if a.dtype != np.float32:
+        raise TypeError("expected float32-convertible input")
+    return a
+
+
+def recurrence(q, k, v, S0=None, nthreads: int | None = None, _lib_obj=None):
+    """Causal linear attention by the token-by-token fp64 recurrence.
+
+    q, k, v: arrays of shape [..., N, d] holding fp32 (or bf16-valued fp32)
+    numbers; the leading axes enumerate independent (batch, head) pairs.
+    S0: optional [..., d, d] initial state (zeros when omitted).
+    Returns (o, S_N): o float64 [..., N, d] and S_N float64 [..., d, d].
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    if not (q.shape == k.shape == v.shape) or q.ndim < 2:
+        raise ValueError(f"q, k, v must share a shape [..., N, d]; got {q.shape}, {k.shape}, {v.shape}")
+    *lead, N, d = q.shape
+    nheads = int(np.prod(lead)) if lead else 1
+    if S0 is None:
+        S = np.zeros((*lead, d, d), dtype=np.float64)
+    else:
+        S = np.array(S0, dtype=np.float64, order="C", copy=True)
+        if S.shape != (*lead, d, d):
+            raise ValueError(f"S0 must have shape {(*lead, d, d)}; got {S.shape}")
+    o = np.empty((*lead, N, d), dtype=np.float64)
+    if nheads == 0 or N == 0:
+        return o, S
+    lib = _lib_obj if _lib_obj is not None else _load()
+    rc = lib.lao_recurrence(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data,
+                            S.ctypes.data, nheads, N, d, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle recurrence failed with code {rc}")
+    return o, S
+
+
+def decode_step(q, k, v, S, nthreads: int | None = None):
+    """One decode token per head: S <- S + k v^T ; o = q^T S (fp64, in place
+    on the float64 array ``S``).  q, k, v: [..., d]; S: [..., d, d] float64.
+    Returns o float64 [..., d]."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    if not isinstance(S, np.ndarray) or S.dtype != np.float64 or not S.flags.c_contiguous:
+        raise TypeError("S must be a C-contiguous float64 array (updated in place)")
+    *lead, d = q.shape
+    if S.shape != (*lead, d, d):
+        raise ValueError(f"S must have shape {(*lead, d, d)}; got {S.shape}")
+    nheads = int(np.prod(lead)) if lead else 1
+    o = np.empty((*lead, d), dtype=np.float64)
+    if nheads == 0:
+        return o
+    rc = _load().lao_recurrence(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data,
+                                S.ctypes.data, nheads, 1, d, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle decode failed with code {rc}")
+    return o
+
+
+def decode_step_bf16_state(q, k, v, S_bits, nthreads: int | None = None):
+    """One decode token per head with the state kept in bf16 between steps.
+
+    S_bits: uint16 array [..., d, d] of bf16 bit patterns, updated in place:
+    widened to double, S += k v^T, o = q^T S read from the double value, then
+    stored back rounded to nearest-even bf16.  Returns o float64 [..., d]."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    if not isinstance(S_bits, np.ndarray) or S_bits.dtype != np.uint16 or not S_bits.flags.c_contiguous:
+        raise TypeError("S_bits must be a C-contiguous uint16 array (updated in place)")
+    *lead, d = q.shape
+    if S_bits.shape != (*lead, d, d):
+        raise ValueError(f"S_bits must have shape {(*lead, d, d)}; got {S_bits.shape}")
+    nheads = int(np.prod(lead)) if lead else 1
+    o = np.empty((*lead, d), dtype=np.float64)
+    if nheads == 0:
+        return o
+    rc = _load().lao_decode_bf16_state(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data,
+                                       S_bits.ctypes.data, nheads, d, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle bf16-state decode failed with code {rc}")
+    return o
+
+
+def round_bf16_bits(x) -> np.ndarray:
+    """Round float64 values to bf16 (nearest, ties to even); uint16 bit patterns."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().lao_round_bf16(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float64 (a bit shift)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
