@@ -1,0 +1,143 @@
+/*
+ * lin_attn.h -- C ABI of the MI355X (gfx950) causal linear-attention library.
+ *
+ * The operation.  Causal linear attention with the identity feature map, as
+ * defined by its recurrent form in "MiniMax-M1で理解する：大規模言語モデルの
+ * コンテキスト長限界を突破する革新的アーキテクチャ" (zenn.dev/liushuzhi),
+ * section "線形アテンションの数学的基礎", recurrence equations:
+ *
+ *     S_t = S_{t-1} + k_t v_t^T            (S in R^{d x d}, fp32)
+ *     o_t = q_t^T S_t                      (the token's own k_t v_t^T included)
+ *
+ * computed in "Lightning" tiles ("Почему M2 в итоге стала моделью с полным
+ * вниманием?" (ai.flicky.cc), section 1, glossary entry "Lightning
+ * Attention": a masked matrix product inside each block and a K^T V state
+ * carried between blocks):
+ *
+ *     O_b = (Q_b K_b^T ⊙ M) V_b + Q_b S_{b-1},   S_b = S_{b-1} + K_b^T V_b,
+ *
+ * with M[r][c] = 1 iff c <= r.  The block size changes rounding and speed,
+ * never the mathematical result.  No feature map other than the identity, no
+ * decay, no normaliser and no 1/sqrt(d) scale is applied.
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers q, k, v, o and state are DEVICE pointers (hipMalloc or
+ *    torch-allocated memory on the current HIP device).  The caller owns
+ *    every buffer; the library allocates nothing and keeps no per-call state.
+ *  - Layouts are dense and row-major: q, k, v, o are [B][H][N][d] (decode:
+ *    [B][H][d]); the state is [B][H][d][d] with row i = key feature and
+ *    column j = value feature.  Each (b, h) pair is an independent sequence.
+ *  - Every base pointer must be 16-byte aligned.  o must not alias q, k or v;
+ *    state must not alias any other argument.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous: they enqueue kernels on `stream` and return; o and state
+ *    hold the results once that stream has been synchronised.
+ *  - All argument checks happen on the host before any HIP call, so a bad
+ *    argument returns an error code without touching the device.  Nothing is
+ *    thrown across the ABI.  A call with zero work (B*H*N == 0) returns
+ *    LIN_ATTN_OK and leaves every buffer untouched.
+ *  - The library is reentrant; concurrent calls on different streams are
+ *    independent as long as their buffers do not overlap.
+ */
+#ifndef LIN_ATTN_H
+#define LIN_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v, o (and of the decode state). */
+typedef enum {
+  LIN_ATTN_F32 = 0,  /* IEEE binary32 */
+  LIN_ATTN_BF16 = 1  /* bfloat16; conversions round to nearest, ties to even */
+} lin_attn_dtype_t;
+
+/* Return codes. */
+enum {
+  LIN_ATTN_OK = 0,
+  LIN_ATTN_EINVAL = -1,       /* null pointer with work to do, negative size, misaligned pointer */
+  LIN_ATTN_EUNSUPPORTED = -2, /* valid request outside what the kernels implement (d, block, dtype) */
+  LIN_ATTN_EHIP = -3          /* the HIP runtime reported an error (launch or device query) */
+};
+
+/*
+ * Chunked ("Lightning") prefill over whole sequences.
+ *
+ * q, k, v : [B][H][N][d] of io_dtype (read only)
+ * o       : [B][H][N][d] of io_dtype (written)
+ * state   : [B][H][d][d] fp32, IN: S_0 of every sequence, OUT: S_N (in place)
+ * block   : tokens per tile.  N need not be a multiple of block; the last
+ *           tile of each sequence is partial.
+ *
+ * Supported: d in {64, 128}.
+ *   io_dtype BF16: block a multiple of 16 with 16 <= block <= 128 (d = 128)
+ *                  or <= 256 (d = 64).  All four products run on bf16 MFMA
+ *                  with fp32 accumulation; the intra-block matrix and the
+ *                  state operand are rounded to bf16, the state itself is
+ *                  accumulated in fp32 for the whole sequence.
+ *   io_dtype F32:  block a multiple of 16 with 16 <= block <= 64 (d = 128)
+ *                  or <= 128 (d = 64).  All arithmetic in fp32.
+ * Errors: LIN_ATTN_EINVAL, LIN_ATTN_EUNSUPPORTED as above; LIN_ATTN_EHIP if
+ * the launch fails.
+ */
+int lin_attn_prefill(const void *q, const void *k, const void *v, void *o, float *state,
+                     int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                     lin_attn_dtype_t io_dtype, void *stream);
+
+/*
+ * lin_attn_prefill with an explicit work split.  `split` is the number of
+ * value-column slices each sequence is divided into (one workgroup per
+ * slice; each slice recomputes the block's Q K^T product).  0 lets the
+ * library choose (it splits only while B*H is below the compute-unit count);
+ * otherwise bf16 I/O accepts 1, 2 or 4 (d = 128) and 1 or 2 (d = 64), and fp32
+ * I/O accepts 1.  Results agree with lin_attn_prefill for every split up to
+ * rounding, and are bit-identical across repeated calls with the same split.
+ */
+int lin_attn_prefill_ex(const void *q, const void *k, const void *v, void *o, float *state,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                        lin_attn_dtype_t io_dtype, int64_t split, void *stream);
+
+/*
+ * One decode token per sequence: S <- S + k v^T, then o = q^T S (the
+ * recurrence above with N = 1), for all B*H sequences at once.
+ *
+ * q, k, v : [B][H][d] of io_dtype (read only)
+ * o       : [B][H][d] of io_dtype (written)
+ * state   : [B][H][d][d] of state_dtype, updated in place.  With
+ *           state_dtype = LIN_ATTN_BF16 the state is widened to fp32, updated
+ *           in fp32, o is read from the fp32 value, and the state is stored
+ *           back rounded to bf16 (the low-precision state storage discussed in
+ *           "ノーフリーランチ：MiniMax M2が高効率アテンション機構を解体"
+ *           (winzheng.jp), section "推論システム統合の課題").
+ *
+ * Supported: d in {64, 128}; io_dtype and state_dtype in {F32, BF16}.
+ */
+int lin_attn_decode(const void *q, const void *k, const void *v, void *o, void *state,
+                    int64_t B, int64_t H, int64_t d,
+                    lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
+
+/*
+ * Token-by-token prefill: the recurrence above applied one token at a time
+ * inside one kernel, with the fp32 state held on chip and plain vector FMAs
+ * (4 d^2 flop per token, no matrix cores).  Same arguments, layouts and
+ * results as lin_attn_prefill, without the block argument; it is the
+ * sequential baseline the tiled form is compared against ("ノーフリーランチ"
+ * (winzheng.jp), section "計算とメモリのボトルネックの不整合": the expected
+ * break-even of linear attention at a few thousand tokens).
+ *
+ * Supported: d in {64, 128}; io_dtype in {F32, BF16}.
+ */
+int lin_attn_prefill_recurrent(const void *q, const void *k, const void *v, void *o,
+                               float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                               lin_attn_dtype_t io_dtype, void *stream);
+
+/* Static, human-readable text for a return code (never NULL). */
+const char *lin_attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIN_ATTN_H */

@@ -1,0 +1,25 @@
+"""Causal linear attention ("Lightning" tiled form) for AMD MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels behind the C ABI of
+``include/lin_attn.h``; this package is the thin Python binding over it
+(torch tensors supply device memory and streams) plus the seeded synthetic
+input generator used by the tests and the benchmark (``synth``).
+"""
+from ._binding import (  # noqa: F401
+    BF16,
+    EHIP,
+    EINVAL,
+    EUNSUPPORTED,
+    F32,
+    LIB_PATH,
+    OK,
+    LinAttnError,
+    decode,
+    library,
+    prefill,
+    prefill_recurrent,
+    strerror,
+)
+
+__all__ = ["prefill", "decode", "prefill_recurrent", "strerror", "library", "LinAttnError",
+           "F32", "BF16", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]

@@ -1,0 +1,147 @@
+"""ctypes binding of the C ABI in include/lin_attn.h.
+
+Argument marshalling only: shape/dtype/device checks, pointer extraction and
+the current HIP stream.  Every step of the computation runs in the gfx950
+kernels of ``_lib/liblin_attn.so``; there is no other implementation here,
+and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "liblin_attn.so")
+
+F32, BF16 = 0, 1
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where} failed: {strerror(code)} (code {code})")
+
+
+def library() -> ctypes.CDLL:
+    """Load the HIP library (built by ``python -m linear_attention_lightning_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"HIP library not found at {LIB_PATH}; build it with "
+                    "`python -m linear_attention_lightning_amd.build` (hipcc, gfx950)")
+            lib = ctypes.CDLL(LIB_PATH)
+            p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+            lib.lin_attn_prefill.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
+            lib.lin_attn_prefill.restype = i32
+            lib.lin_attn_prefill_ex.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, i64, p]
+            lib.lin_attn_prefill_ex.restype = i32
+            lib.lin_attn_decode.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p]
+            lib.lin_attn_decode.restype = i32
+            lib.lin_attn_prefill_recurrent.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
+            lib.lin_attn_prefill_recurrent.restype = i32
+            lib.lin_attn_strerror.argtypes = [i32]
+            lib.lin_attn_strerror.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return library().lin_attn_strerror(int(code)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
+
+
+def _check(t, name: str, shape, dtype, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a HIP device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def prefill(q, k, v, o, state, block: int, *, split: int = 0, stream=None):
+    """Chunked causal linear-attention prefill (``lin_attn_prefill_ex``).
+
+    q, k, v, o: [B, H, N, d] bf16 or fp32 (one dtype for all four), contiguous,
+    on one HIP device; state: [B, H, d, d] fp32, S_0 on entry, S_N on return
+    (in place).  ``split`` = value-column slices per sequence (0 = automatic).
+    Enqueued on ``stream`` (default: the current torch stream)."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check(t, name, (B, H, N, d), q.dtype, q.device)
+    _check(state, "state", (B, H, d, d), torch.float32, q.device)
+    rc = library().lin_attn_prefill_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       state.data_ptr(), B, H, N, d, int(block), _dtype_code(q),
+                                       int(split), _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_prefill")
+    return o
+
+
+def decode(q, k, v, o, state, *, stream=None):
+    """One decode token per sequence (``lin_attn_decode``).
+
+    q, k, v, o: [B, H, d] bf16 or fp32; state: [B, H, d, d] fp32 or bf16,
+    updated in place."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d]")
+    B, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check(t, name, (B, H, d), q.dtype, q.device)
+    _check(state, "state", (B, H, d, d), None, q.device)
+    rc = library().lin_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   state.data_ptr(), B, H, d, _dtype_code(q), _dtype_code(state),
+                                   _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_decode")
+    return o
+
+
+def prefill_recurrent(q, k, v, o, state, *, stream=None):
+    """Token-by-token prefill (``lin_attn_prefill_recurrent``); same tensors
+    as :func:`prefill` without the block size."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check(t, name, (B, H, N, d), q.dtype, q.device)
+    _check(state, "state", (B, H, d, d), torch.float32, q.device)
+    rc = library().lin_attn_prefill_recurrent(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                              state.data_ptr(), B, H, N, d, _dtype_code(q),
+                                              _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_prefill_recurrent")
+    return o

@@ -1,0 +1,54 @@
+// Host-side launch interface of the device kernels (internal to the library;
+// the public ABI is include/lin_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lal {
+
+// Chunked prefill, bf16 I/O.
+struct PrefillArgs {
+  const unsigned short *q, *k, *v;  // bf16 bit patterns, [BH][N][d]
+  unsigned short *o;
+  float *state;                      // [BH][d][d]
+  int64_t N;
+  int blk;
+  int nsplit;   // value-column slices per sequence (d / nsplit columns each)
+  int xcd_map;  // set by the launcher
+};
+int prefill_bf16_max_block(int d);
+int prefill_bf16_max_split(int d);
+hipError_t prefill_bf16_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
+
+// Chunked prefill, fp32 I/O.
+struct PrefillF32Args {
+  const float *q, *k, *v;
+  float *o;
+  float *state;
+  int64_t N;
+  int blk;
+};
+int prefill_f32_max_block(int d);
+hipError_t prefill_f32_launch(PrefillF32Args a, int64_t BH, int d, hipStream_t stream);
+
+// One decode token per sequence.
+struct DecodeArgs {
+  const void *q, *k, *v;
+  void *o;
+  void *state;
+  int64_t BH;
+};
+hipError_t decode_launch(DecodeArgs a, int d, bool io_bf16, bool state_bf16, hipStream_t stream);
+
+// Token-by-token prefill with the state on chip.
+struct RecurrentArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *state;
+  int64_t BH;
+  int64_t N;
+};
+hipError_t recurrent_launch(RecurrentArgs a, int d, bool io_bf16, hipStream_t stream);
+
+}  // namespace lal

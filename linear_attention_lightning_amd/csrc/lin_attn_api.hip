@@ -1,0 +1,138 @@
+// C ABI of the linear-attention library: argument validation and dispatch.
+// The operation and the conventions are documented in include/lin_attn.h.
+//
+// Every check that can reject a call runs on the host before the first HIP
+// call, so invalid arguments never reach the device.
+#include <atomic>
+
+#include "kernels.hpp"
+#include "lin_attn.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool ok_ptr(const void *p) { return p != nullptr && aligned16(p); }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+
+// Number of compute units of the current device, cached per device ordinal.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count(int *out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LIN_ATTN_EHIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return LIN_ATTN_OK;
+    }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    return LIN_ATTN_EHIP;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  *out = c;
+  return LIN_ATTN_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? LIN_ATTN_OK : LIN_ATTN_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int lin_attn_prefill_ex(const void *q, const void *k, const void *v, void *o, float *state,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                        lin_attn_dtype_t io_dtype, int64_t split, void *stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 0 || block < 0 || split < 0) return LIN_ATTN_EINVAL;
+  if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
+  const bool bf16 = io_dtype == LIN_ATTN_BF16;
+  const int max_block = bf16 ? lal::prefill_bf16_max_block((int)d) : lal::prefill_f32_max_block((int)d);
+  if (block < 16 || block > max_block || block % 16 != 0) return LIN_ATTN_EUNSUPPORTED;
+  if (split != 0) {
+    if (!bf16 && split != 1) return LIN_ATTN_EUNSUPPORTED;
+    if (bf16 && (split > lal::prefill_bf16_max_split((int)d) || (split & (split - 1)) != 0))
+      return LIN_ATTN_EUNSUPPORTED;
+  }
+  int64_t BH, total;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &total) || !mul_ok(total, d, &total)) return LIN_ATTN_EINVAL;
+  if (BH == 0 || N == 0) return LIN_ATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (!bf16) {
+    if (BH > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+    lal::PrefillF32Args a{(const float *)q, (const float *)k, (const float *)v, (float *)o, state, N,
+                          (int)block};
+    return from_hip(lal::prefill_f32_launch(a, BH, (int)d, s));
+  }
+
+  int nsplit = (int)split;
+  if (nsplit == 0) {
+    // Enough workgroups to give every compute unit one sequence slice: split
+    // the value columns of each sequence while B*H alone leaves CUs idle.
+    int cus = 0;
+    const int rc = cu_count(&cus);
+    if (rc != LIN_ATTN_OK) return rc;
+    nsplit = 1;
+    while (nsplit < lal::prefill_bf16_max_split((int)d) && BH * nsplit < cus) nsplit *= 2;
+  }
+  if (BH * nsplit > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  lal::PrefillArgs a{(const unsigned short *)q, (const unsigned short *)k, (const unsigned short *)v,
+                     (unsigned short *)o, state, N, (int)block, nsplit, 0};
+  return from_hip(lal::prefill_bf16_launch(a, BH, (int)d, s));
+}
+
+int lin_attn_prefill(const void *q, const void *k, const void *v, void *o, float *state, int64_t B,
+                     int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
+                     void *stream) {
+  return lin_attn_prefill_ex(q, k, v, o, state, B, H, N, d, block, io_dtype, 0, stream);
+}
+
+int lin_attn_decode(const void *q, const void *k, const void *v, void *o, void *state, int64_t B,
+                    int64_t H, int64_t d, lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype,
+                    void *stream) {
+  if (B < 0 || H < 0 || d < 0) return LIN_ATTN_EINVAL;
+  if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (state_dtype != LIN_ATTN_F32 && state_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
+  int64_t BH, total;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, d * d, &total)) return LIN_ATTN_EINVAL;
+  if (BH == 0) return LIN_ATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  if ((BH + 3) / 4 > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  lal::DecodeArgs a{q, k, v, o, state, BH};
+  return from_hip(lal::decode_launch(a, (int)d, io_dtype == LIN_ATTN_BF16, state_dtype == LIN_ATTN_BF16,
+                                     (hipStream_t)stream));
+}
+
+int lin_attn_prefill_recurrent(const void *q, const void *k, const void *v, void *o, float *state,
+                               int64_t B, int64_t H, int64_t N, int64_t d, lin_attn_dtype_t io_dtype,
+                               void *stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return LIN_ATTN_EINVAL;
+  if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
+  int64_t BH, total;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &total) || !mul_ok(total, d, &total)) return LIN_ATTN_EINVAL;
+  if (BH == 0 || N == 0) return LIN_ATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  if (BH * (d / 16) > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  lal::RecurrentArgs a{q, k, v, o, state, BH, N};
+  return from_hip(lal::recurrent_launch(a, (int)d, io_dtype == LIN_ATTN_BF16, (hipStream_t)stream));
+}
+
+const char *lin_attn_strerror(int code) {
+  switch (code) {
+    case LIN_ATTN_OK: return "success";
+    case LIN_ATTN_EINVAL: return "invalid argument (null or misaligned pointer, negative or overflowing size)";
+    case LIN_ATTN_EUNSUPPORTED: return "unsupported configuration (head dim, block size, split or dtype)";
+    case LIN_ATTN_EHIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

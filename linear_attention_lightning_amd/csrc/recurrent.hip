@@ -1,0 +1,115 @@
+// Token-by-token causal linear-attention prefill with the state on chip.
+//
+// The recurrence S_t = S_{t-1} + k_t v_t^T, o_t = q_t^T S_t of
+// "MiniMax-M1で理解する…" (zenn.dev/liushuzhi), section
+// "線形アテンションの数学的基礎", applied one token at a time: 4 d^2 flop per
+// token on the vector ALUs, no matrix cores.  It is the sequential baseline
+// that the tiled kernel is measured against.
+//
+// Value columns of the state are independent, so a workgroup owns one
+// (sequence, 16-column slice): each of its 256 threads keeps d/16 fp32 state
+// entries of one column in registers.  Tokens are processed in batches of 32:
+// q, k and the v slice of a batch are staged in LDS, each thread runs the
+// recurrence over the batch and leaves its partial o_t (a sum over its rows)
+// in LDS, and the partials are then reduced and stored.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lal {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCols = 16;    // value columns per workgroup
+constexpr int kGroups = 16;  // row groups (threads per column)
+constexpr int kTB = 32;      // tokens per batch
+
+template <bool BF16>
+__device__ __forceinline__ float ld(const void *p, size_t i) {
+  if constexpr (BF16)
+    return bf16_bits_to_f32(((const u16 *)p)[i]);
+  else
+    return ((const float *)p)[i];
+}
+
+template <int D, bool IO_BF16>
+__global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
+  constexpr int RPT = D / kGroups;  // state rows per thread
+  __shared__ float2 qk[kTB][D];
+  __shared__ float vv[kTB][kCols];
+  __shared__ float red[kTB][kGroups][kCols + 1];
+
+  const int tid = threadIdx.x;
+  const int jj = tid % kCols;
+  const int rg = tid / kCols;
+  constexpr int nslice = D / kCols;
+  const int64_t bh = blockIdx.x / nslice;
+  const int j0 = (int)(blockIdx.x % nslice) * kCols;
+  const int64_t N = a.N;
+  const size_t base = (size_t)bh * (size_t)N * D;
+  float *Sh = a.state + (size_t)bh * D * D;
+
+  float S[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) S[m] = Sh[(size_t)(rg + kGroups * m) * D + j0 + jj];
+
+  for (int64_t tok0 = 0; tok0 < N; tok0 += kTB) {
+    const int n = (int)((N - tok0) < kTB ? (N - tok0) : kTB);
+    for (int idx = tid; idx < kTB * D; idx += kThreads) {
+      const int tt = idx / D, i = idx % D;
+      float2 x = make_float2(0.f, 0.f);
+      if (tt < n) {
+        const size_t off = base + (size_t)(tok0 + tt) * D + i;
+        x = make_float2(ld<IO_BF16>(a.q, off), ld<IO_BF16>(a.k, off));
+      }
+      qk[tt][i] = x;
+    }
+    for (int idx = tid; idx < kTB * kCols; idx += kThreads) {
+      const int tt = idx / kCols, c = idx % kCols;
+      vv[tt][c] = (tt < n) ? ld<IO_BF16>(a.v, base + (size_t)(tok0 + tt) * D + j0 + c) : 0.f;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < n; ++tt) {
+      const float vj = vv[tt][jj];
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        const float2 x = qk[tt][rg + kGroups * m];
+        S[m] = fmaf(x.y, vj, S[m]);   // S_t = S_{t-1} + k_t v_t^T
+        part = fmaf(x.x, S[m], part);  // partial of q_t^T S_t
+      }
+      red[tt][rg][jj] = part;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < n * kCols; idx += kThreads) {
+      const int tt = idx / kCols, c = idx % kCols;
+      float o = 0.f;
+#pragma unroll
+      for (int r = 0; r < kGroups; ++r) o += red[tt][r][c];
+      const size_t oi = base + (size_t)(tok0 + tt) * D + j0 + c;
+      if constexpr (IO_BF16)
+        ((u16 *)a.o)[oi] = f32_to_bf16_bits(o);
+      else
+        ((float *)a.o)[oi] = o;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) Sh[(size_t)(rg + kGroups * m) * D + j0 + jj] = S[m];
+}
+
+template <int D, bool IO>
+hipError_t go(const RecurrentArgs &a, hipStream_t stream) {
+  const int64_t grid = a.BH * (D / kCols);
+  hipLaunchKernelGGL((recurrent_kernel<D, IO>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t recurrent_launch(RecurrentArgs a, int d, bool io_bf16, hipStream_t stream) {
+  if (d == 128) return io_bf16 ? go<128, true>(a, stream) : go<128, false>(a, stream);
+  if (d == 64) return io_bf16 ? go<64, true>(a, stream) : go<64, false>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lal

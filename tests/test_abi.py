@@ -1,0 +1,148 @@
+"""C-ABI contract checks that need no GPU.
+
+The library must load, export every function that include/lin_attn.h
+declares, and reject bad arguments on the host before any HIP call (so these
+calls are safe on a machine without a device).  No call here passes
+validation with work to do, so no kernel is ever launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_lightning_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lin_attn.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails or returns first
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(lin_attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("lin_attn_prefill", "lin_attn_prefill_ex", "lin_attn_decode",
+              "lin_attn_prefill_recurrent", "lin_attn_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in nm.stdout.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_library_is_gfx950_only(tmp_path):
+    """The device code bundled into the library targets gfx950 and nothing else."""
+    fb = tmp_path / "fatbin.bin"
+    # objcopy rewrites its input unless an output file is named; name a scratch copy
+    subprocess.run(["objcopy", f"--dump-section=.hip_fatbin={fb}", la.LIB_PATH, str(tmp_path / "scratch.so")],
+                   check=True)
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          f"--input={fb}"], capture_output=True, text=True, check=True)
+    targets = [t for t in out.stdout.split() if "amdgcn" in t]
+    assert targets and all(t.endswith("gfx950") for t in targets), out.stdout
+
+
+def test_strerror():
+    assert la.strerror(la.OK) == "success"
+    for c in (la.EINVAL, la.EUNSUPPORTED, la.EHIP):
+        assert la.strerror(c) and la.strerror(c) != "success"
+    assert "unknown" in la.strerror(12345)
+
+
+def prefill(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, s=FAKE, B=1, H=1, N=16, d=128, block=64, dt=la.BF16, split=0):
+    return lib.lin_attn_prefill_ex(q, k, v, o, s, B, H, N, d, block, dt, split, None)
+
+
+def test_prefill_validation_codes():
+    lib = la.library()
+    # negative sizes
+    for kw in ({"B": -1}, {"H": -1}, {"N": -1}, {"d": -1}, {"block": -1}, {"split": -1}):
+        assert prefill(lib, **kw) == la.EINVAL, kw
+    # unsupported head dims, block sizes, dtypes and splits
+    for kw in ({"d": 32}, {"d": 96}, {"d": 256}, {"block": 0}, {"block": 8}, {"block": 40},
+               {"block": 144}, {"d": 128, "block": 256}, {"dt": 7}, {"split": 3}, {"split": 8},
+               {"d": 64, "block": 64, "split": 4}, {"dt": la.F32, "block": 128},
+               {"dt": la.F32, "split": 2}):
+        assert prefill(lib, **kw) == la.EUNSUPPORTED, kw
+    # zero work is a successful no-op, even with null pointers
+    for kw in ({"B": 0}, {"H": 0}, {"N": 0}):
+        assert prefill(lib, q=None, k=None, v=None, o=None, s=None, **kw) == la.OK, kw
+    # null or misaligned pointers with work to do
+    for name in ("q", "k", "v", "o", "s"):
+        assert prefill(lib, **{name: None}) == la.EINVAL, name
+        assert prefill(lib, **{name: MISALIGNED}) == la.EINVAL, name
+    # size products that overflow int64
+    assert prefill(lib, B=1 << 40, H=1 << 30) == la.EINVAL
+
+
+def test_prefill_plain_entry_matches_ex_validation():
+    lib = la.library()
+    assert lib.lin_attn_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 100, 64, la.BF16, None) == la.EUNSUPPORTED
+    assert lib.lin_attn_prefill(None, None, None, None, None, 1, 1, 0, 128, 64, la.BF16, None) == la.OK
+    assert lib.lin_attn_prefill(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 128, 64, la.BF16, None) == la.EINVAL
+
+
+def test_supported_block_sizes_are_accepted_by_validation():
+    """Every supported block passes the size checks: with a null q the call then
+    fails on the pointer check (EINVAL), never on the block (EUNSUPPORTED)."""
+    lib = la.library()
+    for d, maxblk in ((128, 128), (64, 256)):
+        for block in range(16, maxblk + 1, 16):
+            assert prefill(lib, q=None, d=d, block=block) == la.EINVAL, (d, block)
+    for d, maxblk in ((128, 64), (64, 128)):
+        for block in range(16, maxblk + 1, 16):
+            assert prefill(lib, q=None, d=d, block=block, dt=la.F32) == la.EINVAL, (d, block)
+
+
+def test_decode_validation_codes():
+    lib = la.library()
+
+    def dec(q=FAKE, k=FAKE, v=FAKE, o=FAKE, s=FAKE, B=1, H=1, d=128, io=la.BF16, st=la.F32):
+        return lib.lin_attn_decode(q, k, v, o, s, B, H, d, io, st, None)
+
+    assert dec(B=-1) == la.EINVAL
+    assert dec(d=96) == la.EUNSUPPORTED
+    assert dec(io=5) == la.EUNSUPPORTED
+    assert dec(st=5) == la.EUNSUPPORTED
+    assert dec(B=0, q=None, k=None, v=None, o=None, s=None) == la.OK
+    for name in ("q", "k", "v", "o", "s"):
+        assert dec(**{name: None}) == la.EINVAL
+        assert dec(**{name: MISALIGNED}) == la.EINVAL
+
+
+def test_recurrent_validation_codes():
+    lib = la.library()
+
+    def rec(q=FAKE, B=1, H=1, N=8, d=128, io=la.BF16):
+        return lib.lin_attn_prefill_recurrent(q, FAKE, FAKE, FAKE, FAKE, B, H, N, d, io, None)
+
+    assert rec(N=-1) == la.EINVAL
+    assert rec(d=48) == la.EUNSUPPORTED
+    assert rec(io=3) == la.EUNSUPPORTED
+    assert rec(N=0, q=None) == la.OK
+    assert rec(q=None) == la.EINVAL
+    assert rec(q=MISALIGNED) == la.EINVAL
+
+
+def test_binding_rejects_bad_tensors_without_a_device():
+    import torch
+    x = torch.zeros(1, 1, 16, 128, dtype=torch.bfloat16)  # CPU tensor
+    s = torch.zeros(1, 1, 128, 128)
+    with pytest.raises(ValueError):
+        la.prefill(x, x, x, x, s, 64)
+    with pytest.raises(ValueError):
+        la.decode(x[:, :, 0], x[:, :, 0], x[:, :, 0], x[:, :, 0], s)
