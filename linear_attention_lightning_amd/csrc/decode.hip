@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void decode_kernel(DecodeArgs 
   static_assert(RPL % U == 0, "row unroll");
 
   __shared__ float2 qk[kWavesPerBlock][D];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t h = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   const bool valid = h < a.BH;

@@ -82,6 +82,7 @@ int lin_attn_prefill_ex(const void *q, const void *k, const void *v, void *o, fl
     while (nsplit < lal::prefill_bf16_max_split((int)d) && BH * nsplit < cus) nsplit *= 2;
   }
   if (BH * nsplit > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  if (N / block > 0x7ffffff0) return LIN_ATTN_EUNSUPPORTED;  // 32-bit block indices
   lal::PrefillArgs a{(const unsigned short *)q, (const unsigned short *)k, (const unsigned short *)v,
                      (unsigned short *)o, state, N, (int)block, nsplit, 0};
   return from_hip(lal::prefill_bf16_launch(a, BH, (int)d, s));
