@@ -72,11 +72,11 @@ enum {
  *           tile of each sequence is partial.
  *
  * Supported: d in {64, 128}.
- *   io_dtype BF16: block a multiple of 16 with 16 <= block <= 128 (d = 128)
- *                  or <= 256 (d = 64).  All four products run on bf16 MFMA
- *                  with fp32 accumulation; the intra-block matrix and the
- *                  state operand are rounded to bf16, the state itself is
- *                  accumulated in fp32 for the whole sequence.
+ *   io_dtype BF16: block a multiple of 16 with 16 <= block <= 128.  All four
+ *                  products run on bf16 MFMA with fp32 accumulation; the
+ *                  intra-block matrix and the state operand are rounded to
+ *                  bf16, the state itself is accumulated in fp32 for the
+ *                  whole sequence.
  *   io_dtype F32:  block a multiple of 16 with 16 <= block <= 64 (d = 128)
  *                  or <= 128 (d = 64).  All arithmetic in fp32.
  * Errors: LIN_ATTN_EINVAL, LIN_ATTN_EUNSUPPORTED as above; LIN_ATTN_EHIP if

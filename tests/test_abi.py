@@ -100,9 +100,10 @@ def test_supported_block_sizes_are_accepted_by_validation():
     """Every supported block passes the size checks: with a null q the call then
     fails on the pointer check (EINVAL), never on the block (EUNSUPPORTED)."""
     lib = la.library()
-    for d, maxblk in ((128, 128), (64, 256)):
+    for d, maxblk in ((128, 128), (64, 128)):
         for block in range(16, maxblk + 1, 16):
             assert prefill(lib, q=None, d=d, block=block) == la.EINVAL, (d, block)
+        assert prefill(lib, q=None, d=d, block=maxblk + 16) == la.EUNSUPPORTED, d
     for d, maxblk in ((128, 64), (64, 128)):
         for block in range(16, maxblk + 1, 16):
             assert prefill(lib, q=None, d=d, block=block, dt=la.F32) == la.EINVAL, (d, block)

@@ -36,7 +36,7 @@ def integer_case(seed, B, H, N, d):
 @pytest.mark.parametrize("d,block,N,split", [
     (128, 64, 300, 1), (128, 128, 300, 1), (128, 16, 77, 1), (128, 48, 200, 1), (128, 96, 250, 1),
     (128, 128, 257, 2), (128, 64, 190, 4), (128, 112, 129, 4),
-    (64, 64, 300, 1), (64, 256, 600, 1), (64, 32, 95, 2), (64, 208, 430, 2),
+    (64, 64, 300, 1), (64, 128, 600, 1), (64, 32, 95, 2), (64, 112, 430, 2), (64, 80, 333, 1),
 ])
 def test_prefill_bf16_exact_integers(d, block, N, split):
     announce("prefill bf16 exact-integer", d, block, N, split)
@@ -59,7 +59,7 @@ def test_prefill_f32_exact_integers(d, block, N):
 
 @pytest.mark.parametrize("B,H,N,d,block,split", [
     (1, 3, 1000, 128, 64, 0), (2, 2, 777, 128, 128, 1), (1, 2, 500, 128, 128, 2),
-    (1, 2, 500, 128, 128, 4), (2, 3, 700, 64, 64, 1), (1, 2, 513, 64, 256, 2),
+    (1, 2, 500, 128, 128, 4), (2, 3, 700, 64, 64, 1), (1, 2, 513, 64, 128, 2), (1, 2, 300, 128, 96, 0),
     (1, 1, 33, 128, 16, 1), (1, 2, 250, 128, 48, 1), (1, 1, 1, 128, 128, 1), (1, 2, 5, 64, 64, 0),
 ])
 def test_prefill_bf16_random(B, H, N, d, block, split):
