@@ -48,7 +48,10 @@
 namespace lal {
 namespace {
 
-constexpr int kWaves = 8;
+#ifndef LAL_PREFILL_WAVES
+#define LAL_PREFILL_WAVES 4
+#endif
+constexpr int kWaves = LAL_PREFILL_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlkMax = 128;
 
@@ -115,24 +118,55 @@ __device__ __forceinline__ void dma_b128(u32x4 desc, int voff, unsigned lds_base
 }
 #pragma clang diagnostic pop
 
+// LDS byte address of p as a scalar.  The zero added comes from an
+// instruction with side effects, so the sum is formed where it is used rather
+// than kept in a scalar register for the whole kernel.
 __device__ __forceinline__ unsigned lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) const char *)p);
+  unsigned zero;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+  return zero + __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) const char *)p);
 }
 
 // Wait until at most n vector-memory operations of this wave are in flight
 // (they complete in issue order).
 __device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt takes an immediate (6 bits): dispatch over every count
   switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+#define LAL_WAIT_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    LAL_WAIT_CASE(0) LAL_WAIT_CASE(1) LAL_WAIT_CASE(2) LAL_WAIT_CASE(3) LAL_WAIT_CASE(4) LAL_WAIT_CASE(5) LAL_WAIT_CASE(6) LAL_WAIT_CASE(7)
+    LAL_WAIT_CASE(8) LAL_WAIT_CASE(9) LAL_WAIT_CASE(10) LAL_WAIT_CASE(11) LAL_WAIT_CASE(12) LAL_WAIT_CASE(13) LAL_WAIT_CASE(14) LAL_WAIT_CASE(15)
+    LAL_WAIT_CASE(16) LAL_WAIT_CASE(17) LAL_WAIT_CASE(18) LAL_WAIT_CASE(19) LAL_WAIT_CASE(20) LAL_WAIT_CASE(21) LAL_WAIT_CASE(22) LAL_WAIT_CASE(23)
+    LAL_WAIT_CASE(24) LAL_WAIT_CASE(25) LAL_WAIT_CASE(26) LAL_WAIT_CASE(27) LAL_WAIT_CASE(28) LAL_WAIT_CASE(29) LAL_WAIT_CASE(30) LAL_WAIT_CASE(31)
+    LAL_WAIT_CASE(32) LAL_WAIT_CASE(33) LAL_WAIT_CASE(34) LAL_WAIT_CASE(35) LAL_WAIT_CASE(36) LAL_WAIT_CASE(37) LAL_WAIT_CASE(38) LAL_WAIT_CASE(39)
+    LAL_WAIT_CASE(40) LAL_WAIT_CASE(41) LAL_WAIT_CASE(42) LAL_WAIT_CASE(43) LAL_WAIT_CASE(44) LAL_WAIT_CASE(45) LAL_WAIT_CASE(46) LAL_WAIT_CASE(47)
+    LAL_WAIT_CASE(48) LAL_WAIT_CASE(49) LAL_WAIT_CASE(50) LAL_WAIT_CASE(51) LAL_WAIT_CASE(52) LAL_WAIT_CASE(53) LAL_WAIT_CASE(54) LAL_WAIT_CASE(55)
+    LAL_WAIT_CASE(56) LAL_WAIT_CASE(57) LAL_WAIT_CASE(58) LAL_WAIT_CASE(59) LAL_WAIT_CASE(60) LAL_WAIT_CASE(61) LAL_WAIT_CASE(62) LAL_WAIT_CASE(63)
+#undef LAL_WAIT_CASE
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;  // never looser than asked
   }
+}
+
+// This lane's index within the wavefront, from an instruction the compiler
+// treats as having side effects, so values derived from it are computed where
+// they are used instead of being kept live across loops.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl<0, N>(f);
 }
 
 template <int D, int DV, int NT>
@@ -150,9 +184,11 @@ struct Plan {
   static constexpr int CG = CG0 < NJ ? CG0 : NJ;
   static constexpr int NJC = NJ / CG;
   static constexpr int AWAVES = RG * CG;
-  // phase B: 4 x 2 grid of waves over the state tiles
-  static constexpr int BIT = NI / 4;
-  static constexpr int BJT = NJ / 2;
+  // phase B: PBR x PBC grid of waves over the state tiles
+  static constexpr int PBR = kWaves < 4 ? kWaves : 4;
+  static constexpr int PBC = kWaves / PBR;
+  static constexpr int BIT = NI / PBR;
+  static constexpr int BJT = NJ / PBC;
   // direct loads: 512 elements (1 KiB) per wave instruction
   static constexpr int KRPI = 512 / D;
   static constexpr int VRPI = 512 / DV;
@@ -165,7 +201,11 @@ struct Plan {
   static constexpr int VI_W = (VINST + kWaves - 1) / kWaves;
   static constexpr int N_DMA = KI_W + VI_W;
   static_assert(KI_W * kWaves * KRPI <= kBlkMax && VI_W * kWaves * VRPI <= kBlkMax, "padding slots stay in the tile");
-  static_assert(N_DMA <= 8, "vmcnt immediate");
+  static_assert(N_DMA <= 16, "vmcnt immediate");
+  // Vector-memory issue slots of phase A: the NKC inter-block steps and the
+  // first NCH_MIN key chunks (every row-tile pair has at least that many).
+  static constexpr int NCH_MIN = (NT / 2) / 2 + 1;
+  static constexpr int NSLOT = NKC + NCH_MIN;
   static_assert(NT % 2 == 0 && NT >= 2 && NT <= 8, "2..8 row tiles per block");
   static_assert(NJ % CG == 0 && AWAVES <= kWaves, "phase A grid");
   static_assert(BIT >= 1 && BJT >= 1, "phase B grid");
@@ -173,7 +213,7 @@ struct Plan {
 };
 
 template <int D, int DV, int NT>
-__global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_bf16_kernel(PrefillArgs a) {
   using P = Plan<D, DV, NT>;
   // Two stages of K and V tiles, and the bf16 copy of the state slice.
   __shared__ __attribute__((aligned(1024))) u16 Ks0[kBlkMax * D];
@@ -225,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   constexpr int VRB = DV * 2;  // bytes per V-slice row
 
   // ---- phase B ownership: i-tiles [ib*BIT, +BIT) x j-tiles [jb*BJT, +BJT) ----
-  const int ib = wave & 3, jb = wave >> 2;
+  const int ib = wave % P::PBR, jb = wave / P::PBR;
   f32x4 S_acc[P::BIT][P::BJT];
 #pragma unroll
   for (int x = 0; x < P::BIT; ++x)
@@ -236,28 +276,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         S_acc[x][y][e] = Sh[(size_t)((ib * P::BIT + x) * 16 + 4 * g + e) * D + (jb * P::BJT + y) * 16 + lr];
 
   // ---- phase A role: row tiles {rg, NT-1-rg} x value tiles [jc0, jc0 + NJC) ----
-  const bool act = wave < P::AWAVES;
+  const bool act = P::AWAVES == kWaves || wave < P::AWAVES;
   const int rg = wave % P::RG;
   const int jc0 = (wave / P::RG) * P::NJC;
 
-  // ---- lane-constant LDS byte offsets ----
+  // ---- per-lane LDS byte offsets ----
   // Every tile row used below is a multiple of 16 plus a lane-dependent part,
   // and the swizzle only looks at the low 4 row bits, so each access is a
-  // per-lane constant plus a compile-time row offset (an immediate).
-  const int h = (lr & 3) >> 1, lo8 = 8 * (lr & 1);
-  const int rr = 4 * g + (lr >> 2);  // row of a transposing read within 16
-  int kfrag[P::NKC];                 // 16-byte fragment of row lr, chunk 4kc+g
-#pragma unroll
-  for (int kc = 0; kc < P::NKC; ++kc) kfrag[kc] = lr * RB + (swz<P::CPRK>(lr, 4 * kc + g) << 4);
-  int vtrA[P::NJC];  // V^T operand of value tile jc0+jl
-#pragma unroll
-  for (int jl = 0; jl < P::NJC; ++jl) vtrA[jl] = rr * VRB + (swz<P::CPRV>(rr, 2 * (jc0 + jl) + h) << 4) + lo8;
-  int ktrB[P::BIT], vtrB[P::BJT];  // K^T and V operands of phase B
-#pragma unroll
-  for (int x = 0; x < P::BIT; ++x) ktrB[x] = rr * RB + (swz<P::CPRK>(rr, 2 * (ib * P::BIT + x) + h) << 4) + lo8;
-#pragma unroll
-  for (int y = 0; y < P::BJT; ++y) vtrB[y] = rr * VRB + (swz<P::CPRV>(rr, 2 * (jb * P::BJT + y) + h) << 4) + lo8;
-  const int qlane = (lr * D + 8 * g) * 2;  // Q fragment of row lr
+  // per-lane part plus a compile-time row offset (an immediate).  The
+  // per-lane parts are recomputed (a few integer operations) from a lane id
+  // the compiler cannot hoist, where they are used: keeping all of them live
+  // across the block loop would cost ~40 registers the matrix pipeline needs.
+  struct LaneOff {
+    int lr, g, h, lo8, rr;
+  };
+  auto lane_off = [&]() __attribute__((always_inline)) {
+    const int ln = lane_now();
+    LaneOff o;
+    o.lr = ln & 15;
+    o.g = ln >> 4;
+    o.h = (o.lr & 3) >> 1;
+    o.lo8 = 8 * (o.lr & 1);
+    o.rr = 4 * o.g + (o.lr >> 2);  // row of a transposing read within 16
+    return o;
+  };
+  // 16-byte fragment of row lr, chunk 4kc+g (K rows and the state copy)
+  auto kfrag = [&](const LaneOff &o, int kc) { return o.lr * RB + (swz<P::CPRK>(o.lr, 4 * kc + o.g) << 4); };
+  // transposing-read operand of value tile jt (V) and key tile it (K^T)
+  auto vtr = [&](const LaneOff &o, int jt) { return o.rr * VRB + (swz<P::CPRV>(o.rr, 2 * jt + o.h) << 4) + o.lo8; };
+  auto ktr = [&](const LaneOff &o, int it) { return o.rr * RB + (swz<P::CPRK>(o.rr, 2 * it + o.h) << 4) + o.lo8; };
 
   auto ld128 = [](const u16 *base, int off) { return *(const bf16x8 *)((const char *)base + off); };
   auto ldtr = [](const u16 *base, int off0, int off1) {
@@ -266,6 +313,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
   };
 
   auto write_state_copy = [&]() {
+    const LaneOff lo = lane_off();
+    const int lr = lo.lr, g = lo.g;
 #pragma unroll
     for (int x = 0; x < P::BIT; ++x)
 #pragma unroll
@@ -278,93 +327,150 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
 
   // ---- Q rows of the wave's two row tiles (registers) ----
   bf16x8 bq[2][P::NKC], qn[2][P::NKC];
-  auto load_q = [&](auto rgi, int64_t tok0, int len) __attribute__((always_inline)) {
-    constexpr int T[2] = {decltype(rgi)::value, NT - 1 - decltype(rgi)::value};
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh + (size_t)tok0 * D, len * D * 2);
+  // Row tiles of the wave's pair: T0 = rg and T1 = NT-1-rg.  Waves without
+  // phase-A work load and store nothing through zero-size descriptors, so
+  // that every wave issues the same vector-memory operations.
+  const int T0 = rg, T1 = NT - 1 - rg;
+  auto load_q_part = [&](int64_t tok0, int len, int u, int kc) __attribute__((always_inline)) {
+    // descriptor built from scalar-forced words: with the generic builder the
+    // compiler could not prove it uniform and looped over lanes per load
+    const u32x4 dq = raw_desc(qh + (size_t)tok0 * D, act ? (uint32_t)len * D * 2 : 0u);
+    __amdgpu_buffer_rsrc_t rq;
+    __builtin_memcpy(&rq, &dq, sizeof(rq));
+    const LaneOff lo = lane_off();
+    const int qlane = (lo.lr * D + 8 * lo.g) * 2;  // Q fragment of row lr
+    qn[u][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rq, qlane, (16 * (u ? T1 : T0) * D + kc * 32) * 2, 0));
+  };
+  auto load_q = [&](int64_t tok0, int len) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int kc = 0; kc < P::NKC; ++kc)
-        qn[u][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rq, qlane, (16 * T[u] * D + kc * 32) * 2, 0));
+      for (int kc = 0; kc < P::NKC; ++kc) load_q_part(tok0, len, u, kc);
   };
 
   // ---- direct HBM -> LDS loads of the K and V tiles of one block ----
   // Rows past len (a partial last block) and the padding slots read zeros.
-  auto issue_kv = [&](int64_t tok0, int len, u16 *Kd, u16 *Vd) __attribute__((always_inline)) {
-    const u32x4 dk = raw_desc(kh + (size_t)tok0 * D, (uint32_t)len * D * 2);
-    const u32x4 dv = raw_desc(vh + (size_t)tok0 * D, (uint32_t)len * D * 2);
-    const u32x4 none = raw_desc(kh, 0);
-#pragma unroll
-    for (int m = 0; m < P::KI_W; ++m) {
+  // A wave issues N_DMA such loads per block, one at a time (kv_issue), so
+  // that they can be spread over the matrix work of the previous block.
+  struct KvDma {
+    int64_t tok0;
+    int len;
+    u16 *Kd, *Vd;
+  };
+  auto kv_prepare = [&](int64_t tok0, int len, u16 *Kd, u16 *Vd) __attribute__((always_inline)) {
+    return KvDma{tok0, len, Kd, Vd};
+  };
+  // The descriptors are rebuilt for every load (a few scalar operations) so
+  // that none of them occupies scalar registers across the matrix work.
+  auto kv_issue = [&](const KvDma &d, int m) __attribute__((always_inline)) {
+    const int lane = lane_now();
+    unsigned zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    if (m < P::KI_W) {
       const int inst = wave + kWaves * m;
       const int row = inst * P::KRPI + lane / P::CPRK;
       const int c = swz<P::CPRK>(row, lane % P::CPRK);
-      dma_b128(inst < P::KINST ? dk : none, (row * D + c * 8) * 2, lds_addr(Kd + inst * 512));
-    }
-#pragma unroll
-    for (int m = 0; m < P::VI_W; ++m) {
-      const int inst = wave + kWaves * m;
+      const u32x4 desc = raw_desc(kh + (size_t)d.tok0 * D, inst < P::KINST ? (uint32_t)d.len * D * 2 + zero : 0u);
+      dma_b128(desc, (row * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
+    } else {
+      const int inst = wave + kWaves * (m - P::KI_W);
       const int row = inst * P::VRPI + lane / P::CPRV;
       const int c = swz<P::CPRV>(row, lane % P::CPRV);
-      dma_b128(inst < P::VINST ? dv : none, (row * D + j0 + c * 8) * 2, lds_addr(Vd + inst * 512));
+      const u32x4 desc = raw_desc(vh + (size_t)d.tok0 * D, inst < P::VINST ? (uint32_t)d.len * D * 2 + zero : 0u);
+      dma_b128(desc, (row * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
     }
+  };
+  auto kv_issue_all = [&](const KvDma &d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < P::N_DMA; ++m) kv_issue(d, m);
   };
   auto block_len = [&](int jb) { return jb < nfull ? blk : last; };
 
 
   // ---- phase A for row-tile pair {RGI, NT-1-RGI}: output rows ----
-  auto phase_a = [&](auto rgi, int64_t tok0, int len, int nlen, const u16 *Kc, const u16 *Vc)
+  auto phase_a = [&](auto rgi, const u16 *Kc, const u16 *Vc, f32x4 (&acc)[2][P::NJC], auto &&vm_slot)
                      __attribute__((always_inline)) {
-    constexpr int T[2] = {decltype(rgi)::value, NT - 1 - decltype(rgi)::value};
-    f32x4 acc[2][P::NJC];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // inter-block part: O^T += S^T Q^T (each state operand feeds both row tiles)
+    constexpr int T[2] = {decltype(rgi)::value, NT - 1 - decltype(rgi)::value};
+    constexpr int NCH = T[1] / 2 + 1;  // 32-key chunks this pair touches
+
+    // Operands of a 32-key chunk: K rows (A operand of P^T = K Q^T, one
+    // buffer, refilled for the next chunk as soon as this chunk's P products
+    // have been issued) and V^T (A operand of O^T += V^T P^T, two buffers).
+    auto need = [](int cc, int s, int u) constexpr { return 2 * cc + s <= T[u] && cc <= T[u] / 2; };
+    const LaneOff lo = lane_off();
+    int kf[P::NKC], vtrA[P::NJC];
+#pragma unroll
+    for (int kc = 0; kc < P::NKC; ++kc) kf[kc] = kfrag(lo, kc);
+#pragma unroll
+    for (int jl = 0; jl < P::NJC; ++jl) vtrA[jl] = vtr(lo, jc0 + jl);
+    bf16x8 kbuf[2][P::NKC];
+    bf16x8 vbuf[2][P::NJC];
+    auto load_k = [&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (!need(cc, s, 0) && !need(cc, s, 1)) continue;
+#pragma unroll
+        for (int kc = 0; kc < P::NKC; ++kc) kbuf[s][kc] = ld128(Kc, kf[kc] + (32 * cc + 16 * s) * RB);
+      }
+    };
+    auto load_v = [&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+      const int c0 = 32 * cc;
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl)
+        vbuf[cc & 1][jl] = ldtr(Vc, vtrA[jl] + c0 * VRB, vtrA[jl] + (c0 + 16) * VRB);
+    };
+
+    // inter-block part: O^T += S^T Q^T (each state operand feeds both row
+    // tiles).  The state operands of step kc + 1 are requested before the
+    // products of step kc; the first key chunk's operands during the last two.
+    bf16x8 sfr[P::NKC][P::NJC];
+    auto load_s = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) sfr[kc][jl] = ld128(SsT, kf[kc] + (jc0 + jl) * 16 * RB);
+    };
+    load_s(0);
 #pragma unroll
     for (int kc = 0; kc < P::NKC; ++kc) {
+      vm_slot(kc);  // a share of the next block's Q rows and K/V tiles
+      if (kc + 1 < P::NKC) load_s(kc + 1);
+      if (kc == P::NKC - 2 || (P::NKC == 1 && kc == 0)) load_k(std::integral_constant<int, 0>{});
+      if (kc == P::NKC - 1) load_v(std::integral_constant<int, 0>{});
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jl = 0; jl < P::NJC; ++jl) {
-        const bf16x8 as = ld128(SsT, kfrag[kc] + (jc0 + jl) * 16 * RB);
-        acc[0][jl] = mfma_16x16x32(as, bq[0][kc], acc[0][jl]);
-        acc[1][jl] = mfma_16x16x32(as, bq[1][kc], acc[1][jl]);
+        acc[0][jl] = mfma_16x16x32(sfr[kc][jl], bq[0][kc], acc[0][jl]);
+        acc[1][jl] = mfma_16x16x32(sfr[kc][jl], bq[1][kc], acc[1][jl]);
       }
     }
 
     // intra-block part, 32 keys at a time: O^T += V^T (P ⊙ M)^T.  Chunk cc
     // holds keys 32cc .. 32cc+31; row tile t uses chunks 0 .. t/2, and only
     // its last chunk straddles the diagonal.
-#pragma unroll
-    for (int cc = 0; cc <= T[1] / 2; ++cc) {
-      const int c0 = 32 * cc;
-      bf16x8 va[P::NJC];
-#pragma unroll
-      for (int jl = 0; jl < P::NJC; ++jl) va[jl] = ldtr(Vc, vtrA[jl] + c0 * VRB, vtrA[jl] + (c0 + 16) * VRB);
-      // pt[u][s][e] = P[16 T_u + lr][c0 + 16 s + 4g + e]   (P^T = K Q^T)
+    static_for<NCH>([&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (cc < P::NCH_MIN) vm_slot(P::NKC + cc);
+      // pt[u][s][e] = P[16 T_u + lr][32 cc + 16 s + 4g + e]   (P^T = K Q^T)
       f32x4 pt[2][2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bool need0 = cc <= T[0] / 2 && 2 * cc + s <= T[0];
-        const bool need1 = 2 * cc + s <= T[1];
-        if (!need0 && !need1) {
-          pt[0][s] = pt[1][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-          continue;
-        }
-        bf16x8 ka[P::NKC];
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int kc = 0; kc < P::NKC; ++kc) ka[kc] = ld128(Kc, kfrag[kc] + (c0 + 16 * s) * RB);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int s = 0; s < 2; ++s) {
           pt[u][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (u == 0 ? need0 : need1) {
+          if (!need(cc, s, u)) continue;
 #pragma unroll
-            for (int kc = 0; kc < P::NKC; ++kc) pt[u][s] = mfma_16x16x32(ka[kc], bq[u][kc], pt[u][s]);
-          }
+          for (int kc = 0; kc < P::NKC; ++kc) pt[u][s] = mfma_16x16x32(kbuf[s][kc], bq[u][kc], pt[u][s]);
         }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (cc + 1 < NCH) {
+        load_k(std::integral_constant<int, cc + 1>{});
+        load_v(std::integral_constant<int, cc + 1>{});
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (cc > T[u] / 2) continue;
@@ -386,78 +492,114 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
           }
         }
 #pragma unroll
-        for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = mfma_16x16x32(va[jl], pb, acc[u][jl]);
+        for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = mfma_16x16x32(vbuf[cc & 1][jl], pb, acc[u][jl]);
       }
-    }
+    });
 
+  };
+
+  // Call f(integral_constant<int, rg>) for the wave's row-tile pair.
+  // Exactly one call on every path (the last case is unconditional), which
+  // lets the compiler count the memory operations each path issues.
+  auto with_rg = [&](auto &&f) __attribute__((always_inline)) {
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, (P::RG > 1 ? 1 : 0)>;
+    using I2 = std::integral_constant<int, (P::RG > 2 ? 2 : 0)>;
+    using I3 = std::integral_constant<int, (P::RG > 3 ? 3 : 0)>;
+    if constexpr (P::RG == 1) {
+      f(I0{});
+    } else if constexpr (P::RG == 2) {
+      if (rg == 0) f(I0{}); else f(I1{});
+    } else if constexpr (P::RG == 3) {
+      if (rg == 0) f(I0{}); else if (rg == 1) f(I1{}); else f(I2{});
+    } else {
+      if (rg == 0) f(I0{}); else if (rg == 1) f(I1{}); else if (rg == 2) f(I2{}); else f(I3{});
+    }
+  };
+
+  // ---- output rows of the wave's pair: acc[u][jl][e] =
+  // O[16 T_u + lr][(jc0 + jl) * 16 + 4g + e].  Rows past len fall outside the
+  // descriptor and are dropped, so every wave issues the same stores. ----
+  auto store_o_part = [&](int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jl)
+                          __attribute__((always_inline)) {
+    const u32x4 dod = raw_desc(oh + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
+    __amdgpu_buffer_rsrc_t ro;
+    __builtin_memcpy(&ro, &dod, sizeof(ro));
+    // The row-tile part of the offset goes in the scalar offset, so each
+    // lane needs one address register for all of these stores.
+    const LaneOff lo_st = lane_off();
+    const int olane = (lo_st.lr * D + jc0 * 16 + 4 * lo_st.g) * 2;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, packed[u][jl]), ro, olane + jl * 32,
+                                          16 * (u ? T1 : T0) * D * 2, 0);
+  };
+
+  // ---- one block.  On entry the direct loads of block jblk (into Kc, Vc)
+  // and its Q rows (issued interleaved), then the output stores of block
+  // jblk-1, may be in flight; the other stage (Kn, Vn) is free (its block's
+  // reads ended at the previous block's second barrier).  During the block
+  // the wave issues, spread over its matrix work so that no burst stalls it
+  // on a full memory queue: the Q rows and K/V tiles of block jblk+1 (in
+  // phase A) and this block's output stores (in phase B). ----
+  auto body = [&](int jblk, const u16 *Kc, const u16 *Vc, u16 *Kn, u16 *Vn) __attribute__((always_inline)) {
+    const int64_t tok0 = (int64_t)jblk * blk;
+    const int len = block_len(jblk);
+    const int nlen = jblk + 1 < nblk ? block_len(jblk + 1) : 0;
+    // Wait for this block's tiles and Q rows; the previous block's 2 NJC
+    // output stores, issued after them, may stay in flight.
+    wait_vmcnt(jblk == 0 ? 0 : 2 * P::NJC);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kc = 0; kc < P::NKC; ++kc) bq[u][kc] = qn[u][kc];
+    lds_barrier();  // every wave's tiles of block jblk and the state copy are in LDS
+
+    // the next block's loads, one share per issue slot
+    const KvDma dma = kv_prepare(tok0 + blk, nlen, Kn, Vn);
+    auto vm_slot = [&](int slot) __attribute__((always_inline)) {
+      if (slot < P::NKC) {
+        load_q_part(tok0 + blk, nlen, 0, slot);
+        load_q_part(tok0 + blk, nlen, 1, slot);
+      }
+      if (nlen > 0) {
+#pragma unroll
+        for (int m = slot * P::N_DMA / P::NSLOT; m < (slot + 1) * P::N_DMA / P::NSLOT; ++m) kv_issue(dma, m);
+      }
+    };
+
+    // ---------------- phase A: output rows ----------------
+    f32x4 acc[2][P::NJC];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (act) {
+      with_rg([&](auto rgi) { phase_a(rgi, Kc, Vc, acc, vm_slot); });
+    } else {
+#pragma unroll
+      for (int slot = 0; slot < P::NSLOT; ++slot) vm_slot(slot);
+    }
     uint2 packed[2][P::NJC];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int jl = 0; jl < P::NJC; ++jl) packed[u][jl] = pack_bf16x4(acc[u][jl]);
 
-    // The next block's Q rows, issued only now so that their registers are not
-    // live during the products above, and before this block's output stores,
-    // so that waiting for them later leaves the stores' latency hidden.
-    __builtin_amdgcn_sched_barrier(0);
-    load_q(rgi, tok0 + blk, nlen);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // store: acc[u][jl][e] = O[16 T_u + lr][(jc0 + jl) * 16 + 4g + e].  Rows
-    // past len fall outside the descriptor and are dropped, so every wave
-    // issues the same stores on every block.
-    const u32x4 dod = raw_desc(oh + (size_t)tok0 * D, (uint32_t)(len * D - j0) * 2);
-    __amdgpu_buffer_rsrc_t ro;
-    __builtin_memcpy(&ro, &dod, sizeof(ro));
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r = 16 * T[u] + lr;
-#pragma unroll
-      for (int jl = 0; jl < P::NJC; ++jl)
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, packed[u][jl]), ro, ((r * D + (jc0 + jl) * 16 + 4 * g) * 2), 0, 0);
-    }
-  };
-
-  // Call f(integral_constant<int, rg>) for the wave's row-tile pair.
-  auto with_rg = [&](auto &&f) __attribute__((always_inline)) {
-    if (rg == 0) f(std::integral_constant<int, 0>{});
-    if constexpr (P::RG > 1) if (rg == 1) f(std::integral_constant<int, (P::RG > 1 ? 1 : 0)>{});
-    if constexpr (P::RG > 2) if (rg == 2) f(std::integral_constant<int, (P::RG > 2 ? 2 : 0)>{});
-    if constexpr (P::RG > 3) if (rg == 3) f(std::integral_constant<int, (P::RG > 3 ? 3 : 0)>{});
-  };
-
-  // ---- one block.  On entry the direct loads of block jblk (into Kc, Vc)
-  // and, if it exists, of block jblk+1 (into the other stage) are in flight.
-  // On exit the loads of block jblk+2 into (Kc, Vc) have been issued. ----
-  auto body = [&](int jblk, const u16 *Kc, const u16 *Vc) __attribute__((always_inline)) {
-    const int64_t tok0 = (int64_t)jblk * blk;
-    const int len = block_len(jblk);
-    // Everything issued before block jblk+1's direct loads (the last N_DMA
-    // vector-memory operations of this wave, if that block exists) has
-    // landed: this block's K/V tiles, its Q rows and the previous block's
-    // output stores.
-    if (jblk + 1 < nblk)
-      wait_vmcnt(P::N_DMA);
-    else
-      wait_vmcnt(0);
-    if (act) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int kc = 0; kc < P::NKC; ++kc) bq[u][kc] = qn[u][kc];
-    }
-    lds_barrier();  // every wave's tiles of block jblk and the state copy are in LDS
-
-    // ---------------- phase A: output rows (and the next block's Q) ----------------
-    if (act) {
-      const int nlen = jblk + 1 < nblk ? block_len(jblk + 1) : 0;
-      with_rg([&](auto rgi) { phase_a(rgi, tok0, len, nlen, Kc, Vc); });
-    }
-
     // ---------------- phase B: state update S += K^T V ----------------
+    // (with this block's output stores spread over its chunks)
+    const LaneOff lob = lane_off();
+    int ktrB[P::BIT], vtrB[P::BJT];  // K^T and V operands of phase B
+#pragma unroll
+    for (int x = 0; x < P::BIT; ++x) ktrB[x] = ktr(lob, ib * P::BIT + x);
+#pragma unroll
+    for (int y = 0; y < P::BJT; ++y) vtrB[y] = vtr(lob, jb * P::BJT + y);
 #pragma unroll
     for (int cc = 0; cc < P::NCC; ++cc) {
       const int c0 = 32 * cc;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = cc * 2 * P::NJC / P::NCC; i < (cc + 1) * 2 * P::NJC / P::NCC; ++i)
+        store_o_part(tok0, len, packed, i / P::NJC, i % P::NJC);
+      __builtin_amdgcn_sched_barrier(0);
       bf16x8 ka[P::BIT], vb[P::BJT];
 #pragma unroll
       for (int x = 0; x < P::BIT; ++x) ka[x] = ldtr(Kc, ktrB[x] + c0 * RB, ktrB[x] + (c0 + 16) * RB);
@@ -469,27 +611,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_bf16_kernel(PrefillArgs a
         for (int y = 0; y < P::BJT; ++y) S_acc[x][y] = mfma_16x16x32(ka[x], vb[y], S_acc[x][y]);
     }
 
-    // Every wave's reads of this stage and of the state copy are complete.
-    // Only LDS accesses are drained: waiting for vector memory here would
-    // also wait for block jblk+1's loads, which are still in flight.
+    // Every wave's reads of this stage and of the state copy are complete
+    // (only LDS accesses are drained, not the loads in flight).
     lds_barrier();
     write_state_copy();  // bf16 copy of S_jblk for the next block's phase A
-    // Refill this stage with block jblk+2 while the LDS is otherwise idle.
-    if (jblk + 2 < nblk) issue_kv(tok0 + 2 * (int64_t)blk, block_len(jblk + 2), (u16 *)Kc, (u16 *)Vc);
   };
 
   {
     const int len0 = block_len(0);
-    if (act) with_rg([&](auto rgi) { load_q(rgi, 0, len0); });
-    // The initial state is consumed here, before the loop, so the compiler's
-    // waits for its loads stay out of the pipelined loop.
+    kv_issue_all(kv_prepare(0, len0, Ks0, Vs0));
+    load_q(0, len0);
+    // The initial state and the first Q rows are consumed here, before the
+    // loop, so the compiler's waits for their loads stay out of the
+    // pipelined loop (where they would drain the loads in flight).
     write_state_copy();
-    issue_kv(0, len0, Ks0, Vs0);
-    if (nblk > 1) issue_kv(blk, block_len(1), Ks1, Vs1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kc = 0; kc < P::NKC; ++kc) asm volatile("" ::"v"(qn[u][kc]));
   }
   for (int jblk = 0; jblk < nblk; jblk += 2) {
-    body(jblk, Ks0, Vs0);
-    if (jblk + 1 < nblk) body(jblk + 1, Ks1, Vs1);
+    body(jblk, Ks0, Vs0, Ks1, Vs1);
+    if (jblk + 1 < nblk) body(jblk + 1, Ks1, Vs1, Ks0, Vs0);
   }
 
   // ---- final state ----
