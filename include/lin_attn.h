@@ -133,6 +133,27 @@ int lin_attn_prefill_recurrent(const void *q, const void *k, const void *v, void
                                float *state, int64_t B, int64_t H, int64_t N, int64_t d,
                                lin_attn_dtype_t io_dtype, void *stream);
 
+/*
+ * State accumulation over a token segment: state <- state + K^T V, i.e. the
+ * state update of the recurrence above applied to N tokens, without q and
+ * without outputs.  Summed in front of a later segment, the result is that
+ * segment's initial state: a sequence cut into segments processed
+ * independently is recombined by exclusive prefix sums of their K^T V
+ * (the decomposition implied by the associativity equation of [ZENN],
+ * section "線形アテンションの数学的基礎").
+ *
+ * k, v  : [B][H][N][d] of io_dtype (read only)
+ * state : [B][H][d][d] fp32, updated in place (start from zero to obtain
+ *         K^T V alone)
+ *
+ * Supported: d in {64, 128}; io_dtype in {F32, BF16}.  bf16 products run on
+ * matrix cores with fp32 accumulation; the result is deterministic (fixed
+ * summation order, no atomics).
+ */
+int lin_attn_state_accumulate(const void *k, const void *v, float *state,
+                              int64_t B, int64_t H, int64_t N, int64_t d,
+                              lin_attn_dtype_t io_dtype, void *stream);
+
 /* Static, human-readable text for a return code (never NULL). */
 const char *lin_attn_strerror(int code);
 

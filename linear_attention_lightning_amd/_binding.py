@@ -46,6 +46,8 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_decode.restype = i32
             lib.lin_attn_prefill_recurrent.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
             lib.lin_attn_prefill_recurrent.restype = i32
+            lib.lin_attn_state_accumulate.argtypes = [p, p, p, i64, i64, i64, i64, i32, p]
+            lib.lin_attn_state_accumulate.restype = i32
             lib.lin_attn_strerror.argtypes = [i32]
             lib.lin_attn_strerror.restype = ctypes.c_char_p
             _lib = lib
@@ -145,3 +147,22 @@ def prefill_recurrent(q, k, v, o, state, *, stream=None):
     if rc != OK:
         raise LinAttnError(rc, "lin_attn_prefill_recurrent")
     return o
+
+
+def state_accumulate(k, v, state, *, stream=None):
+    """state += K^T V over the N tokens of k, v (``lin_attn_state_accumulate``).
+
+    k, v: [B, H, N, d] bf16 or fp32 (same dtype); state: [B, H, d, d] fp32,
+    updated in place."""
+    import torch
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, N, d]")
+    B, H, N, d = k.shape
+    _check(v, "v", (B, H, N, d), k.dtype, k.device)
+    _check(k, "k", (B, H, N, d), k.dtype, k.device)
+    _check(state, "state", (B, H, d, d), torch.float32, k.device)
+    rc = library().lin_attn_state_accumulate(k.data_ptr(), v.data_ptr(), state.data_ptr(), B, H, N, d,
+                                             _dtype_code(k), _stream(stream, k.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_state_accumulate")
+    return state

@@ -51,4 +51,19 @@ struct RecurrentArgs {
 };
 hipError_t recurrent_launch(RecurrentArgs a, int d, bool io_bf16, hipStream_t stream);
 
+// State accumulation over a token segment: state += K^T V (no q, no outputs).
+struct StateDeltaArgs {
+  const unsigned short *k, *v;  // bf16 bit patterns, [BH][N][d]
+  float *state;                 // [BH][d][d]
+  int64_t N;
+  int xcd_map;  // set by the launcher
+};
+hipError_t state_delta_launch(StateDeltaArgs a, int64_t BH, int d, hipStream_t stream);
+struct StateDeltaF32Args {
+  const float *k, *v;
+  float *state;
+  int64_t N;
+};
+hipError_t state_delta_f32_launch(StateDeltaF32Args a, int64_t BH, int d, hipStream_t stream);
+
 }  // namespace lal

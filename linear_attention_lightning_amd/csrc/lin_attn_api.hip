@@ -126,6 +126,27 @@ int lin_attn_prefill_recurrent(const void *q, const void *k, const void *v, void
   return from_hip(lal::recurrent_launch(a, (int)d, io_dtype == LIN_ATTN_BF16, (hipStream_t)stream));
 }
 
+int lin_attn_state_accumulate(const void *k, const void *v, float *state, int64_t B, int64_t H, int64_t N,
+                              int64_t d, lin_attn_dtype_t io_dtype, void *stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return LIN_ATTN_EINVAL;
+  if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
+  int64_t BH, total;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &total) || !mul_ok(total, d, &total)) return LIN_ATTN_EINVAL;
+  if (BH == 0 || N == 0) return LIN_ATTN_OK;
+  if (!ok_ptr(k) || !ok_ptr(v) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  const int64_t tiles = (d / 64) * (d / 64);
+  if (BH * tiles > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  // 32-bit descriptor ranges: one staged tile of 128 tokens spans < 2^31 bytes
+  hipStream_t s = (hipStream_t)stream;
+  if (io_dtype == LIN_ATTN_BF16) {
+    lal::StateDeltaArgs a{(const unsigned short *)k, (const unsigned short *)v, state, N, 0};
+    return from_hip(lal::state_delta_launch(a, BH, (int)d, s));
+  }
+  lal::StateDeltaF32Args a{(const float *)k, (const float *)v, state, N};
+  return from_hip(lal::state_delta_f32_launch(a, BH, (int)d, s));
+}
+
 const char *lin_attn_strerror(int code) {
   switch (code) {
     case LIN_ATTN_OK: return "success";

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("lin_attn_prefill", "lin_attn_prefill_ex", "lin_attn_decode",
-              "lin_attn_prefill_recurrent", "lin_attn_strerror"):
+              "lin_attn_prefill_recurrent", "lin_attn_state_accumulate", "lin_attn_strerror"):
         assert n in names
 
 
@@ -147,3 +147,21 @@ def test_binding_rejects_bad_tensors_without_a_device():
         la.prefill(x, x, x, x, s, 64)
     with pytest.raises(ValueError):
         la.decode(x[:, :, 0], x[:, :, 0], x[:, :, 0], x[:, :, 0], s)
+
+
+def test_state_accumulate_validation_codes():
+    lib = la.library()
+
+    def acc(k=FAKE, v=FAKE, s=FAKE, B=1, H=1, N=8, d=128, io=la.BF16):
+        return lib.lin_attn_state_accumulate(k, v, s, B, H, N, d, io, None)
+
+    for kw in ({"B": -1}, {"H": -1}, {"N": -1}, {"d": -1}):
+        assert acc(**kw) == la.EINVAL, kw
+    for kw in ({"d": 32}, {"d": 96}, {"io": 4}):
+        assert acc(**kw) == la.EUNSUPPORTED, kw
+    for kw in ({"B": 0}, {"H": 0}, {"N": 0}):
+        assert acc(k=None, v=None, s=None, **kw) == la.OK, kw
+    for name in ("k", "v", "s"):
+        assert acc(**{name: None}) == la.EINVAL, name
+        assert acc(**{name: MISALIGNED}) == la.EINVAL, name
+    assert acc(B=1 << 40, H=1 << 30) == la.EINVAL
