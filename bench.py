@@ -38,6 +38,8 @@ METRIC = "prefill tokens/s + TFLOP/s (% bf16 MFMA peak); decode state GB/s (% HB
 PREFILL = dict(B=4, H=64, N=32768, d=128, block=128)
 DECODE = dict(B=256, H=64, d=128)
 SMALL = dict(B=1, H=8, N=4096, d=128, block=64)
+# one GPU's share of the 1M-token sequence cut into 8 segments (sequence sharding)
+SHARD = dict(B=1, H=64, N=131072, d=128, block=128)
 
 PREFILL_KERNEL_SOURCES = ["linear_attention_lightning_amd/csrc/prefill_bf16.hip",
                           "linear_attention_lightning_amd/csrc/common.hpp"]
@@ -60,6 +62,12 @@ def prefill_flops(B, H, N, d, block, **_):
 def prefill_dense_flops(B, H, N, d, block, **_):
     """Flop as the matrix cores execute them (full masked tiles)."""
     return B * H * N * (4 * d * d + 4 * d * block)
+
+
+def state_accumulate_bytes(B, H, N, d, **_):
+    """bf16 k and v read once (4 d bytes per token-head) plus the fp32 state
+    read and written once per sequence."""
+    return B * H * (N * 4 * d + 8 * d * d)
 
 
 def decode_bytes(B, H, d, state_bytes):
@@ -127,7 +135,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy"],
                     help="run one kernel only (for counter collection); prints timings, no JSON")
     args = ap.parse_args()
 
@@ -161,7 +169,8 @@ def main():
 
     P, D, S = PREFILL, DECODE, SMALL
     need = {"prefill": args.only in (None, "prefill"), "decode": args.only in (None, "decode"),
-            "small": args.only in (None, "recurrent")}
+            "small": args.only in (None, "recurrent"), "shard": args.only in (None, "shard")}
+    SH = SHARD
     t_setup = time.time()
     if need["prefill"]:
         pq, pk, pv = synth.prefill_inputs_device(3, P["B"], P["H"], P["N"], P["d"])
@@ -179,12 +188,20 @@ def main():
         so2 = torch.empty_like(sq)
         sS2 = torch.zeros_like(sS)
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    if need["shard"]:
+        hq, hk, hv = synth.prefill_inputs_device(4, SH["B"], SH["H"], SH["N"], SH["d"])
+        ho = torch.empty_like(hq)
+        # a non-zero initial state: the prefix sum of the earlier segments
+        hS0 = torch.zeros((SH["B"], SH["H"], SH["d"], SH["d"]), dtype=torch.float32, device=dev)
+        la.state_accumulate(hk, hv, hS0)
+        hdS = torch.zeros_like(hS0)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
     names = [n for n, on in (("prefill", need["prefill"]), ("decode_fp32", need["decode"]),
                              ("decode_bf16", need["decode"]), ("small_chunked", need["small"]),
-                             ("small_recurrent", need["small"])) if on]
+                             ("small_recurrent", need["small"]), ("shard_state_accumulate", need["shard"]),
+                             ("shard_prefill", need["shard"])) if on]
 
     def step(evs):
         def timed(name, fn):
@@ -203,6 +220,9 @@ def main():
             timed("small_chunked", lambda: la.prefill(sq, sk, sv, so, sS, S["block"]))
             flush.fill_(1)
             timed("small_recurrent", lambda: la.prefill_recurrent(sq, sk, sv, so2, sS2))
+        if need["shard"]:
+            timed("shard_state_accumulate", lambda: la.state_accumulate(hk, hv, hdS))
+            timed("shard_prefill", lambda: la.prefill(hq, hk, hv, ho, hS0, SH["block"]))
 
     for _ in range(args.warmup):
         step(None)
@@ -283,6 +303,13 @@ def main():
             "chunked_tokens_per_s": small_tokens / (avg["small_chunked"] / 1e3),
             "recurrent_tokens_per_s": small_tokens / (avg["small_recurrent"] / 1e3),
             "cache": "each run follows a 512 MiB write that evicts the 256 MB last-level cache",
+        },
+        "sequence_shard": {
+            "workload": "one of 8 segments of the 1M-token sequence: B=1 H=64 N=131072 d=128, bf16",
+            "state_accumulate_ms": avg["shard_state_accumulate"],
+            "state_accumulate_GBps": state_accumulate_bytes(**SH) / (avg["shard_state_accumulate"] / 1e3) / 1e9,
+            "prefill_nonzero_S0_ms": avg["shard_prefill"],
+            "prefill_nonzero_S0_GBps": prefill_bytes(**SH) / (avg["shard_prefill"] / 1e3) / 1e9,
         },
         "roofline": {
             "bound": "hbm",

@@ -100,6 +100,26 @@ int lin_attn_prefill_ex(const void *q, const void *k, const void *v, void *o, fl
                         lin_attn_dtype_t io_dtype, int64_t split, void *stream);
 
 /*
+ * lin_attn_prefill that also keeps state snapshots for a prefix cache
+ * (resuming a sequence from a stored state is the continuation property of
+ * the recurrence; keeping such states is the prefix-caching concern of
+ * "ノーフリーランチ" (winzheng.jp), section "推論システム統合の課題").
+ *
+ * snapshots : [B][H][nsnap][d][d] fp32, written; nsnap = (N / block) / every
+ *             (integer divisions).  Snapshot s is S_t, the state after the
+ *             first t = (s + 1) * every * block tokens (the initial state
+ *             included), i.e. the state a later prefill of the tokens from t
+ *             on starts from.  May be NULL when nsnap is 0.
+ * every     : blocks between snapshots, >= 1 (else LIN_ATTN_EINVAL).
+ *
+ * All other arguments, results and errors as lin_attn_prefill; o and the
+ * final state are bit-identical to lin_attn_prefill's.
+ */
+int lin_attn_prefill_snapshots(const void *q, const void *k, const void *v, void *o, float *state,
+                               float *snapshots, int64_t B, int64_t H, int64_t N, int64_t d,
+                               int64_t block, int64_t every, lin_attn_dtype_t io_dtype, void *stream);
+
+/*
  * One decode token per sequence: S <- S + k v^T, then o = q^T S (the
  * recurrence above with N = 1), for all B*H sequences at once.
  *

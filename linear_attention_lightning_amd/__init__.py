@@ -18,9 +18,11 @@ from ._binding import (  # noqa: F401
     library,
     prefill,
     prefill_recurrent,
+    prefill_snapshots,
+    snapshot_count,
     state_accumulate,
     strerror,
 )
 
-__all__ = ["prefill", "decode", "prefill_recurrent", "state_accumulate", "strerror", "library", "LinAttnError",
+__all__ = ["prefill", "decode", "prefill_recurrent", "prefill_snapshots", "snapshot_count", "state_accumulate", "strerror", "library", "LinAttnError",
            "F32", "BF16", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]

@@ -46,6 +46,8 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_decode.restype = i32
             lib.lin_attn_prefill_recurrent.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
             lib.lin_attn_prefill_recurrent.restype = i32
+            lib.lin_attn_prefill_snapshots.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
+            lib.lin_attn_prefill_snapshots.restype = i32
             lib.lin_attn_state_accumulate.argtypes = [p, p, p, i64, i64, i64, i64, i32, p]
             lib.lin_attn_state_accumulate.restype = i32
             lib.lin_attn_strerror.argtypes = [i32]
@@ -166,3 +168,33 @@ def state_accumulate(k, v, state, *, stream=None):
     if rc != OK:
         raise LinAttnError(rc, "lin_attn_state_accumulate")
     return state
+
+
+def snapshot_count(N: int, block: int, every: int) -> int:
+    """Number of state snapshots lin_attn_prefill_snapshots writes per sequence."""
+    return (N // block) // every
+
+
+def prefill_snapshots(q, k, v, o, state, snapshots, block: int, every: int, *, stream=None):
+    """:func:`prefill` that also writes state snapshots
+    (``lin_attn_prefill_snapshots``): snapshots[b, h, s] = the state after
+    (s + 1) * every * block tokens; snapshots is [B, H, nsnap, d, d] fp32 with
+    nsnap = snapshot_count(N, block, every)."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check(t, name, (B, H, N, d), q.dtype, q.device)
+    _check(state, "state", (B, H, d, d), torch.float32, q.device)
+    if every < 1:
+        raise ValueError("every must be >= 1")
+    nsnap = snapshot_count(N, block, every)
+    _check(snapshots, "snapshots", (B, H, nsnap, d, d), torch.float32, q.device)
+    rc = library().lin_attn_prefill_snapshots(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                              state.data_ptr(), snapshots.data_ptr() if nsnap else None,
+                                              B, H, N, d, int(block), int(every), _dtype_code(q),
+                                              _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_prefill_snapshots")
+    return o

@@ -16,6 +16,10 @@ struct PrefillArgs {
   int blk;
   int nsplit;   // value-column slices per sequence (d / nsplit columns each)
   int xcd_map;  // set by the launcher
+  // optional state snapshots: snap[bh][s] = S after (s + 1) * snap_every
+  // full blocks, for s < (N / blk) / snap_every (null: none)
+  float *snap;
+  int snap_every;
 };
 int prefill_bf16_max_block(int d);
 int prefill_bf16_max_split(int d);
@@ -28,6 +32,8 @@ struct PrefillF32Args {
   float *state;
   int64_t N;
   int blk;
+  float *snap;  // as in PrefillArgs
+  int snap_every;
 };
 int prefill_f32_max_block(int d);
 hipError_t prefill_f32_launch(PrefillF32Args a, int64_t BH, int d, hipStream_t stream);

@@ -42,11 +42,12 @@ int from_hip(hipError_t e) { return e == hipSuccess ? LIN_ATTN_OK : LIN_ATTN_EHI
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int lin_attn_prefill_ex(const void *q, const void *k, const void *v, void *o, float *state,
-                        int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
-                        lin_attn_dtype_t io_dtype, int64_t split, void *stream) {
+// Shared by the prefill entry points: validation order and dispatch.
+int prefill_impl(const void *q, const void *k, const void *v, void *o, float *state, float *snap,
+                 int64_t every, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                 lin_attn_dtype_t io_dtype, int64_t split, void *stream) {
   if (B < 0 || H < 0 || N < 0 || d < 0 || block < 0 || split < 0) return LIN_ATTN_EINVAL;
   if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
@@ -60,14 +61,21 @@ int lin_attn_prefill_ex(const void *q, const void *k, const void *v, void *o, fl
   }
   int64_t BH, total;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &total) || !mul_ok(total, d, &total)) return LIN_ATTN_EINVAL;
+  // snapshots (every > 0): (N / block) / every of them per sequence
+  if (every < 0 || every > 0x7fffffff) return LIN_ATTN_EINVAL;
+  const int64_t nsnap = every > 0 ? (N / block) / every : 0;
+  int64_t snap_elems;
+  if (!mul_ok(BH, nsnap, &snap_elems) || !mul_ok(snap_elems, d * d, &snap_elems)) return LIN_ATTN_EINVAL;
   if (BH == 0 || N == 0) return LIN_ATTN_OK;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  if (nsnap > 0 && !ok_ptr(snap)) return LIN_ATTN_EINVAL;
+  float *snap_k = nsnap > 0 ? snap : nullptr;
   hipStream_t s = (hipStream_t)stream;
 
   if (!bf16) {
     if (BH > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
     lal::PrefillF32Args a{(const float *)q, (const float *)k, (const float *)v, (float *)o, state, N,
-                          (int)block};
+                          (int)block, snap_k, (int)every};
     return from_hip(lal::prefill_f32_launch(a, BH, (int)d, s));
   }
 
@@ -84,8 +92,25 @@ int lin_attn_prefill_ex(const void *q, const void *k, const void *v, void *o, fl
   if (BH * nsplit > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
   if (N / block > 0x7ffffff0) return LIN_ATTN_EUNSUPPORTED;  // 32-bit block indices
   lal::PrefillArgs a{(const unsigned short *)q, (const unsigned short *)k, (const unsigned short *)v,
-                     (unsigned short *)o, state, N, (int)block, nsplit, 0};
+                     (unsigned short *)o, state, N, (int)block, nsplit, 0, snap_k, (int)every};
   return from_hip(lal::prefill_bf16_launch(a, BH, (int)d, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int lin_attn_prefill_ex(const void *q, const void *k, const void *v, void *o, float *state,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                        lin_attn_dtype_t io_dtype, int64_t split, void *stream) {
+  return prefill_impl(q, k, v, o, state, nullptr, 0, B, H, N, d, block, io_dtype, split, stream);
+}
+
+int lin_attn_prefill_snapshots(const void *q, const void *k, const void *v, void *o, float *state,
+                               float *snapshots, int64_t B, int64_t H, int64_t N, int64_t d,
+                               int64_t block, int64_t every, lin_attn_dtype_t io_dtype, void *stream) {
+  if (every < 1) return LIN_ATTN_EINVAL;
+  return prefill_impl(q, k, v, o, state, snapshots, every, B, H, N, d, block, io_dtype, 0, stream);
 }
 
 int lin_attn_prefill(const void *q, const void *k, const void *v, void *o, float *state, int64_t B,

@@ -254,6 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int nfull = (int)(N / blk);                       // blocks of blk tokens
   const int last = (int)(N - (int64_t)nfull * blk);       // tokens in a final partial block
   const int nblk = nfull + (last > 0 ? 1 : 0);
+  const int nsnap = a.snap ? nfull / a.snap_every : 0;  // state snapshots per sequence
 
   const u16 *qh = a.q + (size_t)bh * (size_t)N * D;
   const u16 *kh = a.k + (size_t)bh * (size_t)N * D;
@@ -609,6 +610,18 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       for (int x = 0; x < P::BIT; ++x)
 #pragma unroll
         for (int y = 0; y < P::BJT; ++y) S_acc[x][y] = mfma_16x16x32(ka[x], vb[y], S_acc[x][y]);
+    }
+
+    // optional snapshot of S after this block (full blocks only)
+    if (nsnap > 0 && (jblk + 1) % a.snap_every == 0 && (jblk + 1) / a.snap_every <= nsnap) {
+      float *sp = a.snap + ((size_t)bh * nsnap + ((jblk + 1) / a.snap_every - 1)) * D * D + j0;
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sp[(size_t)((ib * P::BIT + x) * 16 + 4 * g + e) * D + (jb * P::BJT + y) * 16 + lr] = S_acc[x][y][e];
     }
 
     // Every wave's reads of this stage and of the state copy are complete

@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(PrefillF32Args
   float *Sh = a.state + (size_t)bh * D * D;
 
   for (int idx = tid; idx < D * D; idx += kThreads) Ss[idx] = Sh[idx];
+  const int64_t nsnap = a.snap ? (N / blk) / a.snap_every : 0;
 
   for (int64_t tok0 = 0; tok0 < N; tok0 += blk) {
     const int len = (int)((N - tok0) < blk ? (N - tok0) : blk);
@@ -98,6 +99,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(PrefillF32Args
       float s = 0.f;
       for (int c = 0; c < len; ++c) s = fmaf(Ks[c * C::KSTR + i], Vs[c * D + j], s);
       Ss[idx] += s;
+    }
+    // snapshot of the state after this block (each thread copies the entries
+    // it has just updated)
+    const int64_t nb = tok0 / blk + 1;
+    if (nsnap > 0 && nb % a.snap_every == 0 && nb / a.snap_every <= nsnap) {
+      float *sp = a.snap + ((size_t)bh * nsnap + (nb / a.snap_every - 1)) * D * D;
+      for (int idx = tid; idx < D * D; idx += kThreads) sp[idx] = Ss[idx];
     }
   }
   __syncthreads();

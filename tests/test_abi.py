@@ -165,3 +165,19 @@ def test_state_accumulate_validation_codes():
         assert acc(**{name: None}) == la.EINVAL, name
         assert acc(**{name: MISALIGNED}) == la.EINVAL, name
     assert acc(B=1 << 40, H=1 << 30) == la.EINVAL
+
+
+def test_snapshot_validation_codes():
+    lib = la.library()
+
+    def snp(snap=FAKE, N=256, block=64, every=1, q=FAKE, d=128):
+        return lib.lin_attn_prefill_snapshots(q, FAKE, FAKE, FAKE, FAKE, snap, 1, 1, N, d, block, every,
+                                              la.BF16, None)
+
+    assert snp(every=0) == la.EINVAL
+    assert snp(every=-3) == la.EINVAL
+    assert snp(block=40) == la.EUNSUPPORTED
+    assert snp(snap=None) == la.EINVAL          # 4 snapshots due, no buffer
+    assert snp(snap=MISALIGNED) == la.EINVAL
+    assert snp(q=None) == la.EINVAL
+    assert snp(N=0, q=None, snap=None) == la.OK

@@ -7,6 +7,9 @@ Workloads (q, k ~ N(0, 1/d), v ~ N(0, 1), bf16 inputs, fp32 state):
   * prefill B=1, H=8, N=4096, d=128, block 64      -- every head checked
   * prefill B=4, H=64, N=32768, d=128, block 128   -- 6 sampled heads
   * prefill B=1, H=64, N=1048576, d=128, block 128 -- heads 0, 21, 42, 63
+  * one of 8 segments of that sequence, B=1, H=64, N=131072: the segment's
+    K^T V (state accumulation) and its prefill from a non-zero initial state
+    -- heads 0, 45
   * decode 256 x 64 heads, d=128, 128 steps, state = sum of 2048 outer
     products; fp32 state (gated) and bf16 state (drift reported)
 """
@@ -86,6 +89,33 @@ def test_workload_prefill_4x64x32k_sampled():
 def test_workload_prefill_1m_tokens_sampled():
     announce("workload prefill B1 H64 N1048576 d128 blk128 (heads 0,21,42,63)")
     _check_sampled_prefill(1, 64, 1 << 20, 128, 128, 4, [(0, 0), (0, 21), (0, 42), (0, 63)], "B1 H64 N1M")
+
+
+def test_workload_sequence_shard_sampled():
+    announce("workload sequence shard B1 H64 N131072 d128 blk128 (heads 0,45)")
+    B, H, N, d = 1, 64, 131072, 128
+    heads = [(0, 0), (0, 45)]
+    q, k, v = synth.prefill_inputs_device(6, B, H, N, d)
+    dS = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda")
+    la.state_accumulate(k, v, dS)
+    S0 = torch.randn((B, H, d, d), generator=torch.Generator(device="cuda").manual_seed(6),
+                     device="cuda", dtype=torch.float32)
+    S = S0.clone()
+    o = torch.empty_like(q)
+    la.prefill(q, k, v, o, S, 128)
+    torch.cuda.synchronize()
+    qh, kh, vh = (_heads_to_host(t, heads) for t in (q, k, v))
+    S0h = np.stack([host(S0[b, h]) for b, h in heads])
+    dSh = np.stack([host(dS[b, h]) for b, h in heads])
+    oh = np.stack([host(o[b, h]) for b, h in heads])
+    Sh = np.stack([host(S[b, h]) for b, h in heads])
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    o_ref, S_ref = oracle.recurrence(qh, kh, vh, S0h)
+    _, dS_ref = oracle.recurrence(np.zeros_like(kh), kh, vh)
+    eo, es, ed = rel_err(oh, o_ref), rel_err(Sh, S_ref), rel_err(dSh, dS_ref)
+    print(f"  shard: rel err o={eo:.3e} state={es:.3e} K^T V={ed:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and ed <= TOL_BF16
 
 
 def _decode_heads():
