@@ -40,6 +40,7 @@ DECODE = dict(B=256, H=64, d=128)
 SMALL = dict(B=1, H=8, N=4096, d=128, block=64)
 # one GPU's share of the 1M-token sequence cut into 8 segments (sequence sharding)
 SHARD = dict(B=1, H=64, N=131072, d=128, block=128)
+SNAP_EVERY = 8  # blocks between prefix-cache state snapshots (every 1024 tokens)
 
 PREFILL_KERNEL_SOURCES = ["linear_attention_lightning_amd/csrc/prefill_bf16.hip",
                           "linear_attention_lightning_amd/csrc/common.hpp"]
@@ -176,6 +177,10 @@ def main():
         pq, pk, pv = synth.prefill_inputs_device(3, P["B"], P["H"], P["N"], P["d"])
         po = torch.empty_like(pq)
         pS = torch.zeros((P["B"], P["H"], P["d"], P["d"]), dtype=torch.float32, device=dev)
+        # prefix-cache variant: a state snapshot every SNAP_EVERY blocks
+        pS2 = torch.zeros_like(pS)
+        psnap = torch.empty((P["B"], P["H"], la.snapshot_count(P["N"], P["block"], SNAP_EVERY), P["d"], P["d"]),
+                            dtype=torch.float32, device=dev)
     if need["decode"]:
         dS32 = synth.decode_initial_state_device(D["B"], D["H"], D["d"])
         dS16 = dS32.to(torch.bfloat16)
@@ -198,7 +203,8 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
-    names = [n for n, on in (("prefill", need["prefill"]), ("decode_fp32", need["decode"]),
+    names = [n for n, on in (("prefill", need["prefill"]), ("prefill_snapshots", need["prefill"]),
+                             ("decode_fp32", need["decode"]),
                              ("decode_bf16", need["decode"]), ("small_chunked", need["small"]),
                              ("small_recurrent", need["small"]), ("shard_state_accumulate", need["shard"]),
                              ("shard_prefill", need["shard"])) if on]
@@ -212,6 +218,8 @@ def main():
                 evs[name][1].record(stream)
         if need["prefill"]:
             timed("prefill", lambda: la.prefill(pq, pk, pv, po, pS, P["block"]))
+            timed("prefill_snapshots", lambda: la.prefill_snapshots(pq, pk, pv, po, pS2, psnap, P["block"],
+                                                                    SNAP_EVERY))
         if need["decode"]:
             timed("decode_fp32", lambda: la.decode(dq, dk, dv, do, dS32))
             timed("decode_bf16", lambda: la.decode(dq, dk, dv, do, dS16))
@@ -290,6 +298,9 @@ def main():
             / PEAK_BF16_TFLOPS,
             "hbm_GBps": gbs, "pct_hbm_peak": 100 * gbs / PEAK_HBM_GBS,
             "hbm_floor_ms": p_bytes / (PEAK_HBM_GBS * 1e9) * 1e3,
+            "with_snapshots_ms": avg["prefill_snapshots"],
+            "snapshot_every_tokens": SNAP_EVERY * P["block"],
+            "snapshot_bytes": psnap.numel() * 4,
         },
         "decode": {
             "fp32_state_ms": avg["decode_fp32"], "fp32_state_GBps": d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9,

@@ -139,6 +139,43 @@ int lin_attn_decode(const void *q, const void *k, const void *v, void *o, void *
                     lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
 
 /*
+ * Verification of T draft tokens per sequence (speculative decoding):
+ * o_t = q_t^T S_t for t = 0 .. T-1 with S_t = S + sum_{s <= t} k_s v_s^T,
+ * i.e. the outputs T decode steps would produce, from one read of the state,
+ * which is NOT modified.  Once the caller knows how many drafts each
+ * sequence accepts, lin_attn_decode_commit advances the state by exactly
+ * those ("ノーフリーランチ" (winzheng.jp), section "推論システム統合の課題",
+ * names draft verification and rollback as open problems of linear
+ * attention; here a rollback is simply a commit of 0 tokens).
+ *
+ * q, k, v, o : [B][H][T][d] of io_dtype (o written)
+ * state      : [B][H][d][d] of state_dtype, read only
+ * T          : 0 .. 16 (0 is a no-op; larger values: LIN_ATTN_EUNSUPPORTED)
+ *
+ * Supported: d in {64, 128}; io_dtype and state_dtype in {F32, BF16}.
+ */
+int lin_attn_decode_verify(const void *q, const void *k, const void *v, void *o, const void *state,
+                           int64_t B, int64_t H, int64_t T, int64_t d,
+                           lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
+
+/*
+ * Commit of accepted drafts: S <- S + sum_{t < a_b} k_t v_t^T for every head
+ * of batch entry b, with a_b = accept[b] clamped to [0, T].
+ *
+ * k, v   : [B][H][T][d] of io_dtype (the drafts given to lin_attn_decode_verify)
+ * state  : [B][H][d][d] of state_dtype, updated in place
+ * accept : DEVICE pointer to int32[B], or NULL to accept all T drafts
+ *
+ * With an fp32 state the result is bit-identical to a_b calls of
+ * lin_attn_decode (same operations in the same order); with a bf16 state the
+ * update is done in fp32 and rounded once, at the store.  Errors and limits
+ * as lin_attn_decode_verify.
+ */
+int lin_attn_decode_commit(const void *k, const void *v, void *state, const int32_t *accept,
+                           int64_t B, int64_t H, int64_t T, int64_t d,
+                           lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
+
+/*
  * Token-by-token prefill: the recurrence above applied one token at a time
  * inside one kernel, with the fp32 state held on chip and plain vector FMAs
  * (4 d^2 flop per token, no matrix cores).  Same arguments, layouts and

@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     OK,
     LinAttnError,
     decode,
+    decode_commit,
+    decode_verify,
     library,
     prefill,
     prefill_recurrent,
@@ -24,5 +26,5 @@ from ._binding import (  # noqa: F401
     strerror,
 )
 
-__all__ = ["prefill", "decode", "prefill_recurrent", "prefill_snapshots", "snapshot_count", "state_accumulate", "strerror", "library", "LinAttnError",
+__all__ = ["prefill", "decode", "decode_verify", "decode_commit", "prefill_recurrent", "prefill_snapshots", "snapshot_count", "state_accumulate", "strerror", "library", "LinAttnError",
            "F32", "BF16", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]

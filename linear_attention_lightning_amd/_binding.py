@@ -48,6 +48,10 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_prefill_recurrent.restype = i32
             lib.lin_attn_prefill_snapshots.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
             lib.lin_attn_prefill_snapshots.restype = i32
+            lib.lin_attn_decode_verify.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
+            lib.lin_attn_decode_verify.restype = i32
+            lib.lin_attn_decode_commit.argtypes = [p, p, p, p, i64, i64, i64, i64, i32, i32, p]
+            lib.lin_attn_decode_commit.restype = i32
             lib.lin_attn_state_accumulate.argtypes = [p, p, p, i64, i64, i64, i64, i32, p]
             lib.lin_attn_state_accumulate.restype = i32
             lib.lin_attn_strerror.argtypes = [i32]
@@ -198,3 +202,43 @@ def prefill_snapshots(q, k, v, o, state, snapshots, block: int, every: int, *, s
     if rc != OK:
         raise LinAttnError(rc, "lin_attn_prefill_snapshots")
     return o
+
+
+def decode_verify(q, k, v, o, state, *, stream=None):
+    """Outputs of T draft tokens per sequence from one read of the state
+    (``lin_attn_decode_verify``); the state is not modified.
+
+    q, k, v, o: [B, H, T, d] bf16 or fp32; state: [B, H, d, d] fp32 or bf16."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check(t, name, (B, H, T, d), q.dtype, q.device)
+    _check(state, "state", (B, H, d, d), None, q.device)
+    rc = library().lin_attn_decode_verify(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                          state.data_ptr(), B, H, T, d, _dtype_code(q), _dtype_code(state),
+                                          _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_decode_verify")
+    return o
+
+
+def decode_commit(k, v, state, accept=None, *, stream=None):
+    """state += sum over the first accept[b] drafts of k v^T
+    (``lin_attn_decode_commit``); accept: int32 [B] on the device, or None
+    for all T drafts."""
+    import torch
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, T, d]")
+    B, H, T, d = k.shape
+    _check(v, "v", (B, H, T, d), k.dtype, k.device)
+    _check(state, "state", (B, H, d, d), None, k.device)
+    if accept is not None:
+        _check(accept, "accept", (B,), torch.int32, k.device)
+    rc = library().lin_attn_decode_commit(k.data_ptr(), v.data_ptr(), state.data_ptr(),
+                                          accept.data_ptr() if accept is not None else None,
+                                          B, H, T, d, _dtype_code(k), _dtype_code(state),
+                                          _stream(stream, k.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_decode_commit")
+    return state

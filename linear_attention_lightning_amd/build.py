@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "liblin_attn.so")
 SOURCES = ["lin_attn_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "recurrent.hip",
-           "state_delta.hip"]
+           "state_delta.hip", "decode_multi.hip"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

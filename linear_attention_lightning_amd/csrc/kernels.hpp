@@ -57,6 +57,21 @@ struct RecurrentArgs {
 };
 hipError_t recurrent_launch(RecurrentArgs a, int d, bool io_bf16, hipStream_t stream);
 
+// Several decode tokens per sequence: verify (outputs, state read only) and
+// commit (state += sum over the accepted drafts of k v^T).
+struct DecodeMultiArgs {
+  const void *q, *k, *v;  // [BH][T][d] of the I/O type
+  void *o;
+  void *state;            // [BH][d][d]
+  const int32_t *accept;  // [B] accepted drafts per batch entry (commit; null = all T)
+  int64_t BH;
+  int64_t H;
+  int T;
+};
+int decode_multi_max_tokens();
+hipError_t decode_multi_launch(DecodeMultiArgs a, int d, bool commit, bool io_bf16, bool state_bf16,
+                               hipStream_t stream);
+
 // State accumulation over a token segment: state += K^T V (no q, no outputs).
 struct StateDeltaArgs {
   const unsigned short *k, *v;  // bf16 bit patterns, [BH][N][d]

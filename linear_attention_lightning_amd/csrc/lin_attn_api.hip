@@ -151,6 +151,42 @@ int lin_attn_prefill_recurrent(const void *q, const void *k, const void *v, void
   return from_hip(lal::recurrent_launch(a, (int)d, io_dtype == LIN_ATTN_BF16, (hipStream_t)stream));
 }
 
+namespace {
+int decode_multi_impl(const void *q, const void *k, const void *v, void *o, void *state, const int32_t *accept,
+                      bool commit, int64_t B, int64_t H, int64_t T, int64_t d, lin_attn_dtype_t io_dtype,
+                      lin_attn_dtype_t state_dtype, void *stream) {
+  if (B < 0 || H < 0 || T < 0 || d < 0) return LIN_ATTN_EINVAL;
+  if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (state_dtype != LIN_ATTN_F32 && state_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
+  if (T > lal::decode_multi_max_tokens()) return LIN_ATTN_EUNSUPPORTED;
+  int64_t BH, total;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, d * d, &total) || !mul_ok(BH, T * d, &total)) return LIN_ATTN_EINVAL;
+  if (BH == 0 || T == 0) return LIN_ATTN_OK;
+  if ((!commit && (!ok_ptr(q) || !ok_ptr(o))) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(state))
+    return LIN_ATTN_EINVAL;
+  if (accept != nullptr && ((uintptr_t)accept & 3u) != 0) return LIN_ATTN_EINVAL;
+  if ((BH + 1) / 2 > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  lal::DecodeMultiArgs a{q, k, v, o, state, accept, BH, H, (int)T};
+  return from_hip(lal::decode_multi_launch(a, (int)d, commit, io_dtype == LIN_ATTN_BF16,
+                                           state_dtype == LIN_ATTN_BF16, (hipStream_t)stream));
+}
+}  // namespace
+
+int lin_attn_decode_verify(const void *q, const void *k, const void *v, void *o, const void *state, int64_t B,
+                           int64_t H, int64_t T, int64_t d, lin_attn_dtype_t io_dtype,
+                           lin_attn_dtype_t state_dtype, void *stream) {
+  return decode_multi_impl(q, k, v, o, const_cast<void *>(state), nullptr, false, B, H, T, d, io_dtype,
+                           state_dtype, stream);
+}
+
+int lin_attn_decode_commit(const void *k, const void *v, void *state, const int32_t *accept, int64_t B,
+                           int64_t H, int64_t T, int64_t d, lin_attn_dtype_t io_dtype,
+                           lin_attn_dtype_t state_dtype, void *stream) {
+  return decode_multi_impl(nullptr, k, v, nullptr, state, accept, true, B, H, T, d, io_dtype, state_dtype,
+                           stream);
+}
+
 int lin_attn_state_accumulate(const void *k, const void *v, float *state, int64_t B, int64_t H, int64_t N,
                               int64_t d, lin_attn_dtype_t io_dtype, void *stream) {
   if (B < 0 || H < 0 || N < 0 || d < 0) return LIN_ATTN_EINVAL;

@@ -181,3 +181,28 @@ def test_snapshot_validation_codes():
     assert snp(snap=MISALIGNED) == la.EINVAL
     assert snp(q=None) == la.EINVAL
     assert snp(N=0, q=None, snap=None) == la.OK
+
+
+def test_decode_multi_validation_codes():
+    lib = la.library()
+
+    def ver(q=FAKE, o=FAKE, s=FAKE, B=1, H=1, T=4, d=128, io=la.BF16, st=la.F32):
+        return lib.lin_attn_decode_verify(q, FAKE, FAKE, o, s, B, H, T, d, io, st, None)
+
+    def com(k=FAKE, s=FAKE, acc=None, B=1, H=1, T=4, d=128, io=la.BF16, st=la.F32):
+        return lib.lin_attn_decode_commit(k, FAKE, s, acc, B, H, T, d, io, st, None)
+
+    for f in (ver, com):
+        assert f(T=-1) == la.EINVAL
+        assert f(B=-1) == la.EINVAL
+        assert f(T=17) == la.EUNSUPPORTED
+        assert f(d=96) == la.EUNSUPPORTED
+        assert f(io=3) == la.EUNSUPPORTED
+        assert f(st=3) == la.EUNSUPPORTED
+        assert f(T=0, s=None) == la.OK
+        assert f(s=None) == la.EINVAL
+        assert f(s=MISALIGNED) == la.EINVAL
+    assert ver(q=None) == la.EINVAL
+    assert ver(o=MISALIGNED) == la.EINVAL
+    assert com(k=None) == la.EINVAL
+    assert com(acc=FAKE + 2) == la.EINVAL   # accept must be 4-byte aligned
