@@ -41,6 +41,7 @@ SMALL = dict(B=1, H=8, N=4096, d=128, block=64)
 # one GPU's share of the 1M-token sequence cut into 8 segments (sequence sharding)
 SHARD = dict(B=1, H=64, N=131072, d=128, block=128)
 SNAP_EVERY = 8  # blocks between prefix-cache state snapshots (every 1024 tokens)
+DRAFTS = 4      # draft tokens verified per sequence in the speculative step
 
 PREFILL_KERNEL_SOURCES = ["linear_attention_lightning_amd/csrc/prefill_bf16.hip",
                           "linear_attention_lightning_amd/csrc/common.hpp"]
@@ -186,6 +187,11 @@ def main():
         dS16 = dS32.to(torch.bfloat16)
         dq, dk, dv = synth.decode_step_inputs_device(0, D["B"], D["H"], D["d"])
         do = torch.empty_like(dq)
+        # speculative step: DRAFTS drafts per sequence, verified then committed
+        # with per-sequence accepted counts (here: all but the last draft)
+        tq, tk, tv = synth.prefill_inputs_device(7, D["B"], D["H"], DRAFTS, D["d"])
+        to = torch.empty_like(tq)
+        tacc = torch.full((D["B"],), DRAFTS - 1, dtype=torch.int32, device=dev)
     if need["small"]:
         sq, sk, sv = synth.prefill_inputs_device(2, S["B"], S["H"], S["N"], S["d"])
         so = torch.empty_like(sq)
@@ -205,7 +211,8 @@ def main():
 
     names = [n for n, on in (("prefill", need["prefill"]), ("prefill_snapshots", need["prefill"]),
                              ("decode_fp32", need["decode"]),
-                             ("decode_bf16", need["decode"]), ("small_chunked", need["small"]),
+                             ("decode_bf16", need["decode"]), ("verify", need["decode"]),
+                             ("commit", need["decode"]), ("small_chunked", need["small"]),
                              ("small_recurrent", need["small"]), ("shard_state_accumulate", need["shard"]),
                              ("shard_prefill", need["shard"])) if on]
 
@@ -223,6 +230,8 @@ def main():
         if need["decode"]:
             timed("decode_fp32", lambda: la.decode(dq, dk, dv, do, dS32))
             timed("decode_bf16", lambda: la.decode(dq, dk, dv, do, dS16))
+            timed("verify", lambda: la.decode_verify(tq, tk, tv, to, dS32))
+            timed("commit", lambda: la.decode_commit(tk, tv, dS32, tacc))
         if need["small"]:
             flush.fill_(0)
             timed("small_chunked", lambda: la.prefill(sq, sk, sv, so, sS, S["block"]))
@@ -308,6 +317,13 @@ def main():
             "bf16_state_ms": avg["decode_bf16"], "bf16_state_GBps": d16_bytes / (avg["decode_bf16"] / 1e3) / 1e9,
             "bf16_state_pct_hbm_peak": 100 * d16_bytes / (avg["decode_bf16"] / 1e3) / 1e9 / PEAK_HBM_GBS,
             "tokens_per_s_fp32_state": D["B"] / (avg["decode_fp32"] / 1e3),
+            "speculative": {
+                "drafts": DRAFTS, "accepted": DRAFTS - 1,
+                "verify_ms": avg["verify"], "commit_ms": avg["commit"],
+                "verify_state_GBps": D["B"] * D["H"] * D["d"] ** 2 * 4 / (avg["verify"] / 1e3) / 1e9,
+                "commit_state_GBps": 2 * D["B"] * D["H"] * D["d"] ** 2 * 4 / (avg["commit"] / 1e3) / 1e9,
+                "vs_decode_steps": DRAFTS * avg["decode_fp32"] / (avg["verify"] + avg["commit"]),
+            },
         },
         "crossover": {
             "chunked_ms": avg["small_chunked"], "recurrent_ms": avg["small_recurrent"],
