@@ -37,6 +37,11 @@
  * (winzheng.jp), section "推論システム統合の課題", and section 4 of the
  * ai.flicky.cc digest describe: the state is widened to double, updated,
  * read out, then rounded to bf16 (round to nearest, ties to even) once.
+ *
+ * lao_recurrence_stored_state generalises it: the state is stored every
+ * `block` tokens in bf16 or in OCP FP8 E4M3 (the format those pages name as
+ * the extreme case), with a per-head scale, and the tokens in between run
+ * through the exact recurrence above from the widened store.
  */
 #include <math.h>
 #include <pthread.h>
@@ -113,6 +118,82 @@ static double bf16_to_double(uint16_t b) {
   return (double)f;
 }
 
+/* Round a double to the nearest OCP FP8 E4M3 value ("e4m3fn"), ties to
+ * even, saturating; returns the 8-bit code.  Written from the format's
+ * definition: 1 sign bit, 4 exponent bits with bias 7, 3 stored fraction
+ * bits; exponent field 0 holds the subnormals f * 2^-9 (f = 0..7); the code
+ * S.1111.111 is NaN and there is no infinity, so the largest finite value is
+ * 1.75 * 2^8 = 448.  Reading taken for values beyond the range: they are
+ * clamped to +-448 (a stored state must stay finite; the conversion that the
+ * pages' FP8 storage implies is not specified further).  As for bf16, the
+ * value is scaled so that the grid of its binade becomes the integers and
+ * rounded once with rint(). */
+static uint8_t double_to_e4m3_rne_sat(double x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0;
+  if (isnan(x)) return (uint8_t)(sign | 0x7f);
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (a >= 448.0) return (uint8_t)(sign | 0x7e);
+  int e;
+  frexp(a, &e);
+  int unb = e - 1;            /* a in [2^unb, 2^(unb+1)) */
+  if (unb < -6) unb = -6;     /* subnormals share the smallest exponent */
+  double r = rint(ldexp(a, 3 - unb)); /* grid step 2^(unb-3) */
+  double y = ldexp(r, unb - 3);
+  if (y > 448.0) y = 448.0;   /* rounded past the largest finite value */
+  if (y < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)r); /* subnormal, r in 0..7 */
+  frexp(y, &e);
+  unb = e - 1;                                 /* may have moved up a binade */
+  int mant = (int)ldexp(y, 3 - unb);           /* 8 .. 15 */
+  return (uint8_t)(sign | ((unb + 7) << 3) | (mant - 8));
+}
+
+static double e4m3_to_double(uint8_t c) {
+  const int e = (c >> 3) & 15, f = c & 7;
+  double y;
+  if (e == 15 && f == 7) y = NAN;
+  else if (e == 0) y = ldexp((double)f, -9);
+  else y = ldexp((double)(8 + f), e - 10);
+  return (c & 0x80) ? -y : y;
+}
+
+/* A state kept in a narrow format between uses: entry x is stored as the
+ * code of x / scale and read back as value(code) * scale. */
+enum { LAO_FMT_BF16 = 1, LAO_FMT_E4M3 = 2 };
+
+static double stored_to_double(const void *codes, int64_t i, int fmt, double scale) {
+  if (fmt == LAO_FMT_BF16) return bf16_to_double(((const uint16_t *)codes)[i]) * scale;
+  return e4m3_to_double(((const uint8_t *)codes)[i]) * scale;
+}
+
+static void double_to_stored(void *codes, int64_t i, int fmt, double x, double scale) {
+  if (fmt == LAO_FMT_BF16) ((uint16_t *)codes)[i] = double_to_bf16_rne(x / scale);
+  else ((uint8_t *)codes)[i] = double_to_e4m3_rne_sat(x / scale);
+}
+
+/* The recurrence over N tokens with the state stored in a narrow format every
+ * `block` tokens ("ノーフリーランチ" (winzheng.jp), section
+ * "推論システム統合の課題": FP8 or other low-precision storage of a state that
+ * is rewritten again and again).  The stored state is widened, the tokens of
+ * one block run through the exact recurrence from it (so every output of the
+ * block reads the widened carry plus its block's own exact terms), and the
+ * result is rounded back into the store.  block = 1 is the decode step of a
+ * low-precision state; block = N stores only the final state. */
+static void stored_state_one_head(const float *q, const float *k, const float *v,
+                                  double *o, void *codes, int fmt, double scale,
+                                  double *work, int64_t N, int64_t d, int64_t block) {
+  const int64_t dd = d * d;
+  for (int64_t i = 0; i < dd; ++i) work[i] = stored_to_double(codes, i, fmt, scale);
+  for (int64_t t0 = 0; t0 < N; t0 += block) {
+    const int64_t n = (N - t0 < block) ? N - t0 : block;
+    recurrence_one_head(q + t0 * d, k + t0 * d, v + t0 * d, o + t0 * d, work, n, d);
+    for (int64_t i = 0; i < dd; ++i) {
+      double_to_stored(codes, i, fmt, work[i], scale);
+      work[i] = stored_to_double(codes, i, fmt, scale);
+    }
+  }
+}
+
 /* One decode token step per head with the state stored as bf16. */
 static void decode_bf16_state_one_head(const float *q, const float *k,
                                        const float *v, double *o,
@@ -137,12 +218,16 @@ typedef struct {
   int64_t next_head; /* guarded by mu */
   pthread_mutex_t mu;
   int bf16_state;
+  int fmt;              /* stored-state recurrence: LAO_FMT_*, else 0 */
+  void *codes;          /* [nheads][d][d] codes of the stored state */
+  const float *scale;   /* [nheads] or NULL (1.0) */
+  int64_t block;        /* tokens between stores */
 } job_t;
 
 static void *worker(void *arg) {
   job_t *jb = (job_t *)arg;
   double *work = NULL;
-  if (jb->bf16_state) {
+  if (jb->bf16_state || jb->fmt) {
     work = (double *)malloc(sizeof(double) * (size_t)(jb->d * jb->d));
     if (!work) return (void *)1;
   }
@@ -152,7 +237,13 @@ static void *worker(void *arg) {
     pthread_mutex_unlock(&jb->mu);
     if (h >= jb->nheads) break;
     const int64_t td = jb->N * jb->d;
-    if (jb->bf16_state)
+    if (jb->fmt) {
+      const size_t es = jb->fmt == LAO_FMT_BF16 ? 2 : 1;
+      stored_state_one_head(jb->q + h * td, jb->k + h * td, jb->v + h * td, jb->o + h * td,
+                            (char *)jb->codes + (size_t)(h * jb->d * jb->d) * es, jb->fmt,
+                            jb->scale ? (double)jb->scale[h] : 1.0, work, jb->N, jb->d,
+                            jb->block);
+    } else if (jb->bf16_state)
       decode_bf16_state_one_head(jb->q + h * td, jb->k + h * td, jb->v + h * td,
                                  jb->o + h * td, jb->Sb + h * jb->d * jb->d, work,
                                  jb->d);
@@ -238,4 +329,36 @@ int lao_decode_bf16_state(const float *q, const float *k, const float *v,
  * conversion. */
 void lao_round_bf16(const double *x, uint16_t *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = double_to_bf16_rne(x[i]);
+}
+
+/* Recurrence with a state stored in a narrow format every `block` tokens
+ * (and after the last token).
+ * q, k, v : [nheads][N][d] float32 ; o : [nheads][N][d] double (out) ;
+ * codes   : [nheads][d][d] uint16 bf16 patterns (fmt 1) or uint8 OCP E4M3
+ *           codes (fmt 2), in: S_0, out: S_N ;
+ * scale   : [nheads] positive finite, or NULL for 1.0. */
+int lao_recurrence_stored_state(const float *q, const float *k, const float *v, double *o,
+                                void *codes, int fmt, const float *scale, int64_t nheads,
+                                int64_t N, int64_t d, int64_t block, int nthreads) {
+  if (nheads < 0 || N < 0 || d <= 0 || block < 1) return LAO_EINVAL;
+  if (fmt != LAO_FMT_BF16 && fmt != LAO_FMT_E4M3) return LAO_EINVAL;
+  if (nheads == 0 || N == 0) return LAO_OK;
+  if (!q || !k || !v || !o || !codes) return LAO_EINVAL;
+  if (scale)
+    for (int64_t h = 0; h < nheads; ++h)
+      if (!(scale[h] > 0.0f) || isinf(scale[h])) return LAO_EINVAL;
+  job_t jb;
+  memset(&jb, 0, sizeof jb);
+  jb.q = q; jb.k = k; jb.v = v; jb.o = o;
+  jb.nheads = nheads; jb.N = N; jb.d = d;
+  jb.fmt = fmt; jb.codes = codes; jb.scale = scale; jb.block = block;
+  return run_job(&jb, nthreads);
+}
+
+void lao_round_e4m3(const double *x, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = double_to_e4m3_rne_sat(x[i]);
+}
+
+void lao_widen_e4m3(const uint8_t *c, double *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_to_double(c[i]);
 }

@@ -56,6 +56,13 @@ def _bind(path: str):
     lib.lao_decode_bf16_state.restype = ctypes.c_int
     lib.lao_round_bf16.argtypes = [p, p, i64]
     lib.lao_round_bf16.restype = None
+    lib.lao_recurrence_stored_state.argtypes = [p, p, p, p, p, ctypes.c_int, p, i64, i64, i64, i64,
+                                                ctypes.c_int]
+    lib.lao_recurrence_stored_state.restype = ctypes.c_int
+    lib.lao_round_e4m3.argtypes = [p, p, i64]
+    lib.lao_round_e4m3.restype = None
+    lib.lao_widen_e4m3.argtypes = [p, p, i64]
+    lib.lao_widen_e4m3.restype = None
     return lib
 
 
@@ -84,6 +91,26 @@ def compile_variant(src_text: str, out_path: str):
         @staticmethod
         def recurrence(q, k, v, S0=None, nthreads=None):
             return recurrence(q, k, v, S0, nthreads, _lib_obj=lib)
+
+        @staticmethod
+        def round_e4m3_codes(x):
+            return round_e4m3_codes(x, _lib_obj=lib)
+
+        @staticmethod
+        def e4m3_codes_to_f64(codes):
+            return e4m3_codes_to_f64(codes, _lib_obj=lib)
+
+        @staticmethod
+        def round_to_stored(x, fmt, scale=None):
+            return round_to_stored(x, fmt, scale, _lib_obj=lib)
+
+        @staticmethod
+        def stored_to_f64(codes, fmt, scale=None):
+            return stored_to_f64(codes, fmt, scale, _lib_obj=lib)
+
+        @staticmethod
+        def recurrence_stored_state(q, k, v, codes, fmt, scale=None, block=1, nthreads=None):
+            return recurrence_stored_state(q, k, v, codes, fmt, scale, block, nthreads, _lib_obj=lib)
 
     return _Variant()
 
@@ -187,11 +214,11 @@ def decode_step_bf16_state(q, k, v, S_bits, nthreads: int | None = None):
     return o
 
 
-def round_bf16_bits(x) -> np.ndarray:
+def round_bf16_bits(x, _lib_obj=None) -> np.ndarray:
     """Round float64 values to bf16 (nearest, ties to even); uint16 bit patterns."""
     a = np.ascontiguousarray(x, dtype=np.float64)
     out = np.empty(a.shape, dtype=np.uint16)
-    _load().lao_round_bf16(a.ctypes.data, out.ctypes.data, a.size)
+    (_lib_obj or _load()).lao_round_bf16(a.ctypes.data, out.ctypes.data, a.size)
     return out
 
 
@@ -199,3 +226,72 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float64 (a bit shift)."""
     b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+FMT_BF16 = 1
+FMT_E4M3 = 2
+_CODE_DTYPE = {FMT_BF16: np.uint16, FMT_E4M3: np.uint8}
+
+
+def round_e4m3_codes(x, _lib_obj=None) -> np.ndarray:
+    """Round float64 values to OCP FP8 E4M3 (nearest, ties to even, clamped to
+    +-448; NaN stays NaN); uint8 codes."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint8)
+    (_lib_obj or _load()).lao_round_e4m3(a.ctypes.data, out.ctypes.data, a.size)
+    return out
+
+
+def e4m3_codes_to_f64(codes, _lib_obj=None) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 codes as float64 (NaN for S.1111.111)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    (_lib_obj or _load()).lao_widen_e4m3(c.ctypes.data, out.ctypes.data, c.size)
+    return out
+
+
+def stored_to_f64(codes, fmt: int, scale=None, _lib_obj=None) -> np.ndarray:
+    """Value of a stored state: value(code) * scale, scale per head ([...]) or None."""
+    val = bf16_bits_to_f64(codes) if fmt == FMT_BF16 else e4m3_codes_to_f64(codes, _lib_obj)
+    if scale is not None:
+        val = val * np.asarray(scale, dtype=np.float32).astype(np.float64)[..., None, None]
+    return val
+
+
+def round_to_stored(x, fmt: int, scale=None, _lib_obj=None) -> np.ndarray:
+    """Codes of x / scale in the stored format."""
+    x = np.asarray(x, dtype=np.float64)
+    if scale is not None:
+        x = x / np.asarray(scale, dtype=np.float32).astype(np.float64)[..., None, None]
+    return round_bf16_bits(x, _lib_obj) if fmt == FMT_BF16 else round_e4m3_codes(x, _lib_obj)
+
+
+def recurrence_stored_state(q, k, v, codes, fmt: int, scale=None, block: int = 1,
+                            nthreads: int | None = None, _lib_obj=None):
+    """Recurrence whose state is stored in a narrow format every `block`
+    tokens and after the last one.
+
+    codes: C-contiguous [..., d, d] uint16 (fmt FMT_BF16) or uint8 (FMT_E4M3)
+    array, updated in place (in: S_0, out: S_N); scale: float32 [...] per
+    head or None for 1.  Returns o float64 [..., N, d]."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    if fmt not in _CODE_DTYPE:
+        raise ValueError("fmt must be FMT_BF16 or FMT_E4M3")
+    if not isinstance(codes, np.ndarray) or codes.dtype != _CODE_DTYPE[fmt] or not codes.flags.c_contiguous:
+        raise TypeError(f"codes must be a C-contiguous {np.dtype(_CODE_DTYPE[fmt]).name} array (updated in place)")
+    *lead, N, d = q.shape
+    if codes.shape != (*lead, d, d):
+        raise ValueError(f"codes must have shape {(*lead, d, d)}; got {codes.shape}")
+    nheads = int(np.prod(lead)) if lead else 1
+    sc = None
+    if scale is not None:
+        sc = np.ascontiguousarray(np.broadcast_to(np.asarray(scale, dtype=np.float32), tuple(lead)))
+    o = np.empty((*lead, N, d), dtype=np.float64)
+    if nheads == 0 or N == 0:
+        return o
+    rc = (_lib_obj or _load()).lao_recurrence_stored_state(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data,
+                                             codes.ctypes.data, fmt, None if sc is None else sc.ctypes.data,
+                                             nheads, N, d, block, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle stored-state recurrence failed with code {rc}")
+    return o
