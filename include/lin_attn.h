@@ -48,10 +48,15 @@
 extern "C" {
 #endif
 
-/* Element types of q, k, v, o (and of the decode state). */
+/* Element types of q, k, v, o and of a stored state. */
 typedef enum {
-  LIN_ATTN_F32 = 0,  /* IEEE binary32 */
-  LIN_ATTN_BF16 = 1  /* bfloat16; conversions round to nearest, ties to even */
+  LIN_ATTN_F32 = 0,      /* IEEE binary32 */
+  LIN_ATTN_BF16 = 1,     /* bfloat16; conversions round to nearest, ties to even */
+  LIN_ATTN_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("e4m3fn": bias 7, 3 fraction bits, no
+                            infinity, largest finite 448); state storage only.
+                            Conversions round to nearest, ties to even; finite
+                            values beyond +-448 are clamped to +-448; a
+                            non-finite value gets an unspecified code */
 } lin_attn_dtype_t;
 
 /* Return codes. */
@@ -120,6 +125,34 @@ int lin_attn_prefill_snapshots(const void *q, const void *k, const void *v, void
                                int64_t block, int64_t every, lin_attn_dtype_t io_dtype, void *stream);
 
 /*
+ * Chunked prefill with the state stored in a narrow format under a
+ * per-sequence scale (the storage of lin_attn_decode_scaled), for a state
+ * cache that keeps states in bf16 or FP8 between calls.
+ *
+ * state       : [B][H][d][d] of state_dtype (LIN_ATTN_BF16 or
+ *               LIN_ATTN_FP8_E4M3), IN: the stored S_0, OUT: the stored S_N.
+ * state_scale : DEVICE pointer to float[B][H], or NULL (as for
+ *               lin_attn_decode_scaled); the same scale reads S_0 and stores
+ *               S_N.
+ * round_carry : 0: the carry between blocks stays in fp32 and only S_N is
+ *               rounded, on its store.
+ *               1: the carry is rounded to state_dtype after every block
+ *               (the partial last block included), as if the sequence were
+ *               prefilled one block per call with the state stored in between;
+ *               each block's outputs read the rounded carry of the blocks
+ *               before it.
+ *               Other values: LIN_ATTN_EINVAL.
+ *
+ * Everything else as lin_attn_prefill (work split chosen by the library).
+ * Supported: io_dtype BF16 only, d in {64, 128}, block as for bf16 in
+ * lin_attn_prefill.
+ */
+int lin_attn_prefill_scaled(const void *q, const void *k, const void *v, void *o, void *state,
+                            const float *state_scale, int64_t B, int64_t H, int64_t N, int64_t d,
+                            int64_t block, lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype,
+                            int64_t round_carry, void *stream);
+
+/*
  * One decode token per sequence: S <- S + k v^T, then o = q^T S (the
  * recurrence above with N = 1), for all B*H sequences at once.
  *
@@ -132,11 +165,40 @@ int lin_attn_prefill_snapshots(const void *q, const void *k, const void *v, void
  *           "ノーフリーランチ：MiniMax M2が高効率アテンション機構を解体"
  *           (winzheng.jp), section "推論システム統合の課題").
  *
- * Supported: d in {64, 128}; io_dtype and state_dtype in {F32, BF16}.
+ * Supported: d in {64, 128}; io_dtype in {F32, BF16}; state_dtype in {F32,
+ * BF16, FP8_E4M3} (FP8_E4M3 as in lin_attn_decode_scaled with unit scales).
  */
 int lin_attn_decode(const void *q, const void *k, const void *v, void *o, void *state,
                     int64_t B, int64_t H, int64_t d,
                     lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
+
+/*
+ * Decode step with the state stored in a narrow format under a per-sequence
+ * scale (FP8 or other low-precision storage of a state that is rewritten
+ * every token: "ノーフリーランチ" (winzheng.jp), section "推論システム統合の
+ * 課題").
+ *
+ * state       : [B][H][d][d] of state_dtype (LIN_ATTN_BF16 or
+ *               LIN_ATTN_FP8_E4M3), updated in place.  Entry x of sequence
+ *               (b, h) is held as the code of x / scale[b][h]; its value is
+ *               value(code) * scale[b][h].
+ * state_scale : DEVICE pointer to float[B][H], or NULL for 1.0 everywhere.
+ *               Scales must be positive and finite (others give unspecified
+ *               results, never a fault); with powers of two the scaling is
+ *               exact and the result is that of the unscaled computation on
+ *               scaled values.
+ *
+ * Per sequence: the stored state is widened to fp32, S += k v^T in fp32, o is
+ * read from the fp32 value, and the state is stored back rounded to
+ * state_dtype (conversion rules at lin_attn_dtype_t).  lin_attn_decode with
+ * state_dtype BF16 or FP8_E4M3 is this call with state_scale = NULL.
+ *
+ * Supported: d in {64, 128}; io_dtype in {F32, BF16}; state_dtype in {BF16,
+ * FP8_E4M3} (LIN_ATTN_F32: LIN_ATTN_EUNSUPPORTED, use lin_attn_decode).
+ */
+int lin_attn_decode_scaled(const void *q, const void *k, const void *v, void *o, void *state,
+                           const float *state_scale, int64_t B, int64_t H, int64_t d,
+                           lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
 
 /*
  * Verification of T draft tokens per sequence (speculative decoding):

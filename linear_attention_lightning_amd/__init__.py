@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     EINVAL,
     EUNSUPPORTED,
     F32,
+    FP8_E4M3,
     LIB_PATH,
     OK,
     LinAttnError,
@@ -20,11 +21,13 @@ from ._binding import (  # noqa: F401
     library,
     prefill,
     prefill_recurrent,
+    prefill_scaled,
     prefill_snapshots,
     snapshot_count,
     state_accumulate,
     strerror,
 )
 
-__all__ = ["prefill", "decode", "decode_verify", "decode_commit", "prefill_recurrent", "prefill_snapshots", "snapshot_count", "state_accumulate", "strerror", "library", "LinAttnError",
-           "F32", "BF16", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]
+__all__ = ["prefill", "prefill_scaled", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
+           "prefill_snapshots", "snapshot_count", "state_accumulate", "strerror", "library", "LinAttnError",
+           "F32", "BF16", "FP8_E4M3", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]

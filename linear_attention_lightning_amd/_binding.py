@@ -14,7 +14,7 @@ import threading
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lib", "liblin_attn.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 
 _lock = threading.Lock()
@@ -44,6 +44,10 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_prefill_ex.restype = i32
             lib.lin_attn_decode.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p]
             lib.lin_attn_decode.restype = i32
+            lib.lin_attn_decode_scaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i32, i32, p]
+            lib.lin_attn_decode_scaled.restype = i32
+            lib.lin_attn_prefill_scaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, i32, i64, p]
+            lib.lin_attn_prefill_scaled.restype = i32
             lib.lin_attn_prefill_recurrent.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
             lib.lin_attn_prefill_recurrent.restype = i32
             lib.lin_attn_prefill_snapshots.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
@@ -70,7 +74,19 @@ def _dtype_code(t) -> int:
         return BF16
     if t.dtype == torch.float32:
         return F32
-    raise TypeError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}; expected torch.bfloat16, torch.float32 "
+                    "(or torch.float8_e4m3fn for a stored state)")
+
+
+def _scale_ptr(scale, B: int, H: int, device):
+    """Device pointer of a float32 [B, H] scale tensor, or None."""
+    import torch
+    if scale is None:
+        return None
+    _check(scale, "state_scale", (B, H), torch.float32, device)
+    return scale.data_ptr()
 
 
 def _check(t, name: str, shape, dtype, device):
@@ -118,22 +134,59 @@ def prefill(q, k, v, o, state, block: int, *, split: int = 0, stream=None):
     return o
 
 
-def decode(q, k, v, o, state, *, stream=None):
-    """One decode token per sequence (``lin_attn_decode``).
+def decode(q, k, v, o, state, *, state_scale=None, stream=None):
+    """One decode token per sequence (``lin_attn_decode``, or
+    ``lin_attn_decode_scaled`` when ``state_scale`` is given).
 
-    q, k, v, o: [B, H, d] bf16 or fp32; state: [B, H, d, d] fp32 or bf16,
-    updated in place."""
+    q, k, v, o: [B, H, d] bf16 or fp32; state: [B, H, d, d] fp32, bf16 or
+    float8_e4m3fn, updated in place; state_scale: optional float32 [B, H] on
+    the device (narrow states: entry x is stored as x / scale)."""
     if q.dim() != 3:
         raise ValueError("q must be [B, H, d]")
     B, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         _check(t, name, (B, H, d), q.dtype, q.device)
     _check(state, "state", (B, H, d, d), None, q.device)
-    rc = library().lin_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                   state.data_ptr(), B, H, d, _dtype_code(q), _dtype_code(state),
-                                   _stream(stream, q.device))
+    if state_scale is None:
+        rc = library().lin_attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       state.data_ptr(), B, H, d, _dtype_code(q), _dtype_code(state),
+                                       _stream(stream, q.device))
+        where = "lin_attn_decode"
+    else:
+        rc = library().lin_attn_decode_scaled(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                              state.data_ptr(), _scale_ptr(state_scale, B, H, q.device),
+                                              B, H, d, _dtype_code(q), _dtype_code(state),
+                                              _stream(stream, q.device))
+        where = "lin_attn_decode_scaled"
     if rc != OK:
-        raise LinAttnError(rc, "lin_attn_decode")
+        raise LinAttnError(rc, where)
+    return o
+
+
+def prefill_scaled(q, k, v, o, state, block: int, *, state_scale=None, round_carry: bool = False,
+                   stream=None):
+    """Chunked prefill with the state stored as bf16 or float8_e4m3fn codes
+    of state / scale (``lin_attn_prefill_scaled``).
+
+    q, k, v, o: [B, H, N, d] bf16; state: [B, H, d, d] bf16 or
+    float8_e4m3fn, S_0 on entry, S_N on return; state_scale: optional
+    float32 [B, H] on the device; round_carry: round the carry to the
+    state's format after every block."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check(t, name, (B, H, N, d), q.dtype, q.device)
+    _check(state, "state", (B, H, d, d), None, q.device)
+    if state.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise TypeError("state must be bfloat16 or float8_e4m3fn (use prefill for an fp32 state)")
+    rc = library().lin_attn_prefill_scaled(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                           state.data_ptr(), _scale_ptr(state_scale, B, H, q.device),
+                                           B, H, N, d, int(block), _dtype_code(q), _dtype_code(state),
+                                           1 if round_carry else 0, _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_prefill_scaled")
     return o
 
 

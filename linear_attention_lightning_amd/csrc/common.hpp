@@ -66,4 +66,24 @@ __device__ __forceinline__ u16 f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(u16, (bf16)x);
 }
 
+// OCP FP8 E4M3 ("e4m3fn": 1 sign bit, 4 exponent bits with bias 7, 3
+// fraction bits, no infinity, largest finite 448) through gfx950's
+// converters, which round to nearest even.  The converter turns values past
+// the largest finite one into NaN, so finite values are clamped to +-448
+// first (NaN and infinities then store +-448 too).
+__device__ __forceinline__ uint32_t f32_to_e4m3x4(f32x4 x) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(x[0], -448.f, 448.f),
+                                          __builtin_amdgcn_fmed3f(x[1], -448.f, 448.f), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(x[2], -448.f, 448.f),
+                                      __builtin_amdgcn_fmed3f(x[3], -448.f, 448.f), w, true);
+  return (uint32_t)w;  // byte e holds x[e]
+}
+
+// The four codes of a 32-bit word (byte 0 first), widened exactly to fp32.
+__device__ __forceinline__ f32x4 e4m3x4_to_f32(uint32_t w) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return f32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 }  // namespace lal

@@ -7,6 +7,10 @@
 
 namespace lal {
 
+// Storage formats of a state: fp32, or bf16 / OCP FP8 E4M3 codes of
+// state / scale.
+enum StateFmt { kStF32 = 0, kStBF16 = 1, kStE4M3 = 2 };
+
 // Chunked prefill, bf16 I/O.
 struct PrefillArgs {
   const unsigned short *q, *k, *v;  // bf16 bit patterns, [BH][N][d]
@@ -20,10 +24,18 @@ struct PrefillArgs {
   // full blocks, for s < (N / blk) / snap_every (null: none)
   float *snap;
   int snap_every;
+  // narrow-format state (prefill_bf16_scaled_launch; state is then unused):
+  // [BH][d][d] codes of state / scale, per-sequence scales (null = 1), and
+  // whether the carry is rounded to the format after every block
+  void *lp_state;
+  const float *lp_scale;
+  int lp_round;
 };
 int prefill_bf16_max_block(int d);
 int prefill_bf16_max_split(int d);
 hipError_t prefill_bf16_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
+// state_fmt: kStBF16 or kStE4M3
+hipError_t prefill_bf16_scaled_launch(PrefillArgs a, int64_t BH, int d, int state_fmt, hipStream_t stream);
 
 // Chunked prefill, fp32 I/O.
 struct PrefillF32Args {
@@ -42,10 +54,12 @@ hipError_t prefill_f32_launch(PrefillF32Args a, int64_t BH, int d, hipStream_t s
 struct DecodeArgs {
   const void *q, *k, *v;
   void *o;
-  void *state;
+  void *state;         // [BH][d][d] in the storage format
   int64_t BH;
+  const float *scale;  // [BH] per-sequence state scale (narrow formats; null = 1)
 };
-hipError_t decode_launch(DecodeArgs a, int d, bool io_bf16, bool state_bf16, hipStream_t stream);
+// state_fmt: a StateFmt value (common.hpp)
+hipError_t decode_launch(DecodeArgs a, int d, bool io_bf16, int state_fmt, hipStream_t stream);
 
 // Token-by-token prefill with the state on chip.
 struct RecurrentArgs {

@@ -45,9 +45,12 @@ int from_hip(hipError_t e) { return e == hipSuccess ? LIN_ATTN_OK : LIN_ATTN_EHI
 namespace {
 
 // Shared by the prefill entry points: validation order and dispatch.
+// state: fp32 state (lp_fmt == kStF32), else lp_state holds codes of
+// state / lp_scale in the narrow format lp_fmt (bf16 I/O only).
 int prefill_impl(const void *q, const void *k, const void *v, void *o, float *state, float *snap,
                  int64_t every, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
-                 lin_attn_dtype_t io_dtype, int64_t split, void *stream) {
+                 lin_attn_dtype_t io_dtype, int64_t split, void *stream, int lp_fmt = lal::kStF32,
+                 void *lp_state = nullptr, const float *lp_scale = nullptr, int lp_round = 0) {
   if (B < 0 || H < 0 || N < 0 || d < 0 || block < 0 || split < 0) return LIN_ATTN_EINVAL;
   if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
@@ -67,12 +70,16 @@ int prefill_impl(const void *q, const void *k, const void *v, void *o, float *st
   int64_t snap_elems;
   if (!mul_ok(BH, nsnap, &snap_elems) || !mul_ok(snap_elems, d * d, &snap_elems)) return LIN_ATTN_EINVAL;
   if (BH == 0 || N == 0) return LIN_ATTN_OK;
-  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  const bool narrow = lp_fmt != lal::kStF32;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(narrow ? lp_state : (const void *)state))
+    return LIN_ATTN_EINVAL;
+  if (narrow && lp_scale && ((uintptr_t)lp_scale & 3)) return LIN_ATTN_EINVAL;
   if (nsnap > 0 && !ok_ptr(snap)) return LIN_ATTN_EINVAL;
   float *snap_k = nsnap > 0 ? snap : nullptr;
   hipStream_t s = (hipStream_t)stream;
 
   if (!bf16) {
+    if (narrow) return LIN_ATTN_EUNSUPPORTED;
     if (BH > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
     lal::PrefillF32Args a{(const float *)q, (const float *)k, (const float *)v, (float *)o, state, N,
                           (int)block, snap_k, (int)every};
@@ -92,7 +99,9 @@ int prefill_impl(const void *q, const void *k, const void *v, void *o, float *st
   if (BH * nsplit > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
   if (N / block > 0x7ffffff0) return LIN_ATTN_EUNSUPPORTED;  // 32-bit block indices
   lal::PrefillArgs a{(const unsigned short *)q, (const unsigned short *)k, (const unsigned short *)v,
-                     (unsigned short *)o, state, N, (int)block, nsplit, 0, snap_k, (int)every};
+                     (unsigned short *)o, state, N, (int)block, nsplit, 0, snap_k, (int)every,
+                     lp_state, lp_scale, lp_round};
+  if (narrow) return from_hip(lal::prefill_bf16_scaled_launch(a, BH, (int)d, lp_fmt, s));
   return from_hip(lal::prefill_bf16_launch(a, BH, (int)d, s));
 }
 
@@ -113,27 +122,60 @@ int lin_attn_prefill_snapshots(const void *q, const void *k, const void *v, void
   return prefill_impl(q, k, v, o, state, snapshots, every, B, H, N, d, block, io_dtype, 0, stream);
 }
 
+int lin_attn_prefill_scaled(const void *q, const void *k, const void *v, void *o, void *state,
+                            const float *state_scale, int64_t B, int64_t H, int64_t N, int64_t d,
+                            int64_t block, lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype,
+                            int64_t round_carry, void *stream) {
+  if (round_carry != 0 && round_carry != 1) return LIN_ATTN_EINVAL;
+  if (state_dtype != LIN_ATTN_BF16 && state_dtype != LIN_ATTN_FP8_E4M3) return LIN_ATTN_EUNSUPPORTED;
+  if (io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;  // narrow states: bf16 I/O kernel only
+  return prefill_impl(q, k, v, o, nullptr, nullptr, 0, B, H, N, d, block, io_dtype, 0, stream,
+                      state_dtype == LIN_ATTN_BF16 ? lal::kStBF16 : lal::kStE4M3, state, state_scale,
+                      (int)round_carry);
+}
+
 int lin_attn_prefill(const void *q, const void *k, const void *v, void *o, float *state, int64_t B,
                      int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
                      void *stream) {
   return lin_attn_prefill_ex(q, k, v, o, state, B, H, N, d, block, io_dtype, 0, stream);
 }
 
-int lin_attn_decode(const void *q, const void *k, const void *v, void *o, void *state, int64_t B,
-                    int64_t H, int64_t d, lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype,
-                    void *stream) {
+namespace {
+int state_fmt_of(lin_attn_dtype_t t) {
+  return t == LIN_ATTN_F32 ? lal::kStF32 : t == LIN_ATTN_BF16 ? lal::kStBF16 : lal::kStE4M3;
+}
+
+int decode_impl(const void *q, const void *k, const void *v, void *o, void *state, const float *scale,
+                int64_t B, int64_t H, int64_t d, lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype,
+                void *stream) {
   if (B < 0 || H < 0 || d < 0) return LIN_ATTN_EINVAL;
   if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
-  if (state_dtype != LIN_ATTN_F32 && state_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (state_dtype != LIN_ATTN_F32 && state_dtype != LIN_ATTN_BF16 && state_dtype != LIN_ATTN_FP8_E4M3)
+    return LIN_ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
   int64_t BH, total;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, d * d, &total)) return LIN_ATTN_EINVAL;
   if (BH == 0) return LIN_ATTN_OK;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  if (scale && ((uintptr_t)scale & 3)) return LIN_ATTN_EINVAL;
   if ((BH + 3) / 4 > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
-  lal::DecodeArgs a{q, k, v, o, state, BH};
-  return from_hip(lal::decode_launch(a, (int)d, io_dtype == LIN_ATTN_BF16, state_dtype == LIN_ATTN_BF16,
+  lal::DecodeArgs a{q, k, v, o, state, BH, scale};
+  return from_hip(lal::decode_launch(a, (int)d, io_dtype == LIN_ATTN_BF16, state_fmt_of(state_dtype),
                                      (hipStream_t)stream));
+}
+}  // namespace
+
+int lin_attn_decode(const void *q, const void *k, const void *v, void *o, void *state, int64_t B,
+                    int64_t H, int64_t d, lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype,
+                    void *stream) {
+  return decode_impl(q, k, v, o, state, nullptr, B, H, d, io_dtype, state_dtype, stream);
+}
+
+int lin_attn_decode_scaled(const void *q, const void *k, const void *v, void *o, void *state,
+                           const float *state_scale, int64_t B, int64_t H, int64_t d,
+                           lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream) {
+  if (state_dtype == LIN_ATTN_F32) return LIN_ATTN_EUNSUPPORTED;
+  return decode_impl(q, k, v, o, state, state_scale, B, H, d, io_dtype, state_dtype, stream);
 }
 
 int lin_attn_prefill_recurrent(const void *q, const void *k, const void *v, void *o, float *state,

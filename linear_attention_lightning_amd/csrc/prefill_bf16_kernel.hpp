@@ -1,0 +1,770 @@
+// Chunked ("Lightning") causal linear-attention prefill on bf16 matrix cores:
+// the kernel template, included by the translation units that instantiate it.
+//
+// Method: "Почему M2 в итоге стала моделью с полным вниманием?"
+// (ai.flicky.cc), section 1, glossary entry "Lightning Attention" -- linear
+// attention computed in tiles, with a masked matrix product inside each block
+// and a K^T V state carried between blocks -- applied to the recurrence
+// S_t = S_{t-1} + k_t v_t^T, o_t = q_t^T S_t of "MiniMax-M1で理解する…"
+// (zenn.dev/liushuzhi), section "線形アテンションの数学的基礎".  Per block b of
+// `blk` tokens (M[r][c] = 1 iff c <= r):
+//
+//   O_b = (Q_b K_b^T ⊙ M) V_b + Q_b S_{b-1}          (read S before the update)
+//   S_b = S_{b-1} + K_b^T V_b
+//
+// Work decomposition.  One workgroup (4 waves) owns one (batch, head)
+// sequence and a slice of DV value columns [j0, j0 + DV); it walks the blocks
+// of its sequence in order.  The fp32 state slice lives in matrix-core
+// accumulators for the whole sequence and is copied to LDS as bf16 once per
+// block, as the operand of Q_b S.  Slices of one sequence recompute Q_b K_b^T
+// each; they exist to fill the GPU when B*H is small.
+//
+// Data movement (gfx950):
+//  * K and V tiles go HBM -> LDS with buffer_load ... lds (no registers),
+//    double-buffered: block b+1 streams in while block b is computed.  The
+//    buffer descriptor covers exactly the valid rows, so rows past the end of
+//    the sequence arrive as zeros -- ragged tails need no other masking.
+//  * Q rows are loaded by each wave straight into the registers that feed the
+//    matrix cores, one block ahead (issued after the output phase, so that
+//    they occupy registers only during the state update).
+//  * LDS tiles are unpadded with an XOR swizzle of their 16-byte chunks,
+//    chosen so that 16-byte fragment reads (one row per lane) and the
+//    transposing 8-byte reads both run without bank conflicts.
+//
+// Products (all v_mfma_f32_16x16x32_bf16).  Outputs are computed transposed,
+// O^T = S^T Q^T + V^T P^T, so a lane holds four consecutive value features of
+// one token and stores 8 bytes.  P^T = K Q^T lands directly in the B-operand
+// layout of V^T P^T.  K^T and V are read token-major with ds_read_b64_tr_b16.
+//
+// Balance.  Phase A (outputs) pairs row tiles t and NT-1-t so that every
+// wave has the same causal work, and splits value columns across the waves
+// of a pair; phase B (state update) spreads the state over the waves by row
+// tiles.  The number of 16-row tiles per block, NT, is a template parameter
+// so that every loop bound is a compile-time constant.
+//
+// State storage (template parameter SM).  The state that enters and leaves
+// the kernel is fp32, optionally with snapshots of it every few blocks (a
+// prefix cache), or codes of state / scale in bf16 or OCP FP8 E4M3 (a state
+// cache in a narrow format, "ノーフリーランチ" (winzheng.jp), section
+// "推論システム統合の課題").  With a narrow format the carry may also be
+// rounded to it after every block, which is what prefilling one block per
+// call with the state stored in between would compute.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lal {
+namespace {
+
+#ifndef LAL_PREFILL_WAVES
+#define LAL_PREFILL_WAVES 4
+#endif
+constexpr int kWaves = LAL_PREFILL_WAVES;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBlkMax = 128;
+
+enum PrefillStateMode {
+  kPsF32 = 0,      // fp32 state in and out
+  kPsF32Snap = 1,  // fp32 state plus snapshots
+  kPsBF16 = 2,     // bf16 codes of state / scale
+  kPsE4M3 = 3      // OCP FP8 E4M3 codes of state / scale
+};
+
+// Round x / scale to the storage format of SM and return the stored value
+// times scale (exact for power-of-two scales).
+template <int SM>
+__device__ __forceinline__ f32x4 round_to_store(f32x4 x, float sc, float inv) {
+  f32x4 r;
+  if constexpr (SM == kPsBF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (float)(bf16)(x[e] * inv) * sc;
+  } else {
+    const f32x4 y = {x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv};
+    r = e4m3x4_to_f32(f32_to_e4m3x4(y));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] *= sc;
+  }
+  return r;
+}
+
+// Physical 16-byte chunk of logical chunk c in row r of a tile whose rows
+// hold CPR chunks (an involution).
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (CPR == 16)
+    return c ^ ((r & 7) << 1);
+  else if constexpr (CPR == 8)
+    return c ^ ((r >> 1) & 7);
+  else
+    return c ^ ((r >> 2) & 3);
+}
+
+// Element offset of (row r, column col), col a multiple of 4, in such a tile.
+template <int CPR>
+__device__ __forceinline__ int sw_off(int r, int col) {
+  return r * (CPR * 8) + (swz<CPR>(r, col >> 3) << 3) + (col & 7);
+}
+
+// Workgroup barrier that waits only for this wave's outstanding LDS accesses
+// (not for vector-memory loads).  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 8-byte LDS store the compiler does not track.  Its ordering against
+// in-flight direct loads is guaranteed by construction (they target other
+// buffers), and its completion by the lgkmcnt(0) of the next lds_barrier().
+__device__ __forceinline__ void lds_store_b64(const void *lds_ptr, uint2 v) {
+  const unsigned addr = (unsigned)(size_t)(__attribute__((address_space(3))) const char *)lds_ptr;
+  asm volatile("ds_write_b64 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+// Raw buffer descriptor as four scalar words: `bytes` bytes from `base`,
+// stride 0, 32-bit data format; accesses at or past `bytes` read zero.
+__device__ __forceinline__ u32x4 raw_desc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  u32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = 0x00020000u;
+  return d;
+}
+
+// Direct HBM -> LDS load of 16 bytes per lane: lane l's bytes at `voff` in
+// the buffer land at LDS byte address lds_base + 16 l.  Issued from inline
+// assembly so that the compiler does not track it: its own vector-memory
+// waits would otherwise drain these loads before every LDS read, even of
+// other buffers.  Its completion is awaited explicitly with wait_vmcnt()
+// followed by a barrier.  M0 holds the LDS base; one wait state separates its
+// write from the load that reads it.
+// M0 is a reserved register; clobbering it is sound here because nothing else
+// in these kernels keeps a value in M0 (no other LDS-DMA, message or
+// relative-addressing instruction is generated).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_b128(u32x4 desc, int voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte address of p as a scalar.  The zero added comes from an
+// instruction with side effects, so the sum is formed where it is used rather
+// than kept in a scalar register for the whole kernel.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  unsigned zero;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+  return zero + __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) const char *)p);
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (they complete in issue order).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt takes an immediate (6 bits): dispatch over every count
+  switch (n) {
+#define LAL_WAIT_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    LAL_WAIT_CASE(0) LAL_WAIT_CASE(1) LAL_WAIT_CASE(2) LAL_WAIT_CASE(3) LAL_WAIT_CASE(4) LAL_WAIT_CASE(5) LAL_WAIT_CASE(6) LAL_WAIT_CASE(7)
+    LAL_WAIT_CASE(8) LAL_WAIT_CASE(9) LAL_WAIT_CASE(10) LAL_WAIT_CASE(11) LAL_WAIT_CASE(12) LAL_WAIT_CASE(13) LAL_WAIT_CASE(14) LAL_WAIT_CASE(15)
+    LAL_WAIT_CASE(16) LAL_WAIT_CASE(17) LAL_WAIT_CASE(18) LAL_WAIT_CASE(19) LAL_WAIT_CASE(20) LAL_WAIT_CASE(21) LAL_WAIT_CASE(22) LAL_WAIT_CASE(23)
+    LAL_WAIT_CASE(24) LAL_WAIT_CASE(25) LAL_WAIT_CASE(26) LAL_WAIT_CASE(27) LAL_WAIT_CASE(28) LAL_WAIT_CASE(29) LAL_WAIT_CASE(30) LAL_WAIT_CASE(31)
+    LAL_WAIT_CASE(32) LAL_WAIT_CASE(33) LAL_WAIT_CASE(34) LAL_WAIT_CASE(35) LAL_WAIT_CASE(36) LAL_WAIT_CASE(37) LAL_WAIT_CASE(38) LAL_WAIT_CASE(39)
+    LAL_WAIT_CASE(40) LAL_WAIT_CASE(41) LAL_WAIT_CASE(42) LAL_WAIT_CASE(43) LAL_WAIT_CASE(44) LAL_WAIT_CASE(45) LAL_WAIT_CASE(46) LAL_WAIT_CASE(47)
+    LAL_WAIT_CASE(48) LAL_WAIT_CASE(49) LAL_WAIT_CASE(50) LAL_WAIT_CASE(51) LAL_WAIT_CASE(52) LAL_WAIT_CASE(53) LAL_WAIT_CASE(54) LAL_WAIT_CASE(55)
+    LAL_WAIT_CASE(56) LAL_WAIT_CASE(57) LAL_WAIT_CASE(58) LAL_WAIT_CASE(59) LAL_WAIT_CASE(60) LAL_WAIT_CASE(61) LAL_WAIT_CASE(62) LAL_WAIT_CASE(63)
+#undef LAL_WAIT_CASE
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;  // never looser than asked
+  }
+}
+
+// This lane's index within the wavefront, from an instruction the compiler
+// treats as having side effects, so values derived from it are computed where
+// they are used instead of being kept live across loops.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl<0, N>(f);
+}
+
+template <int D, int DV, int NT>
+struct Plan {
+  static constexpr int CPRK = D / 8;   // 16-byte chunks per K row / state-copy row
+  static constexpr int CPRV = DV / 8;  // per V-slice row
+  static constexpr int NJ = DV / 16;
+  static constexpr int NI = D / 16;
+  static constexpr int NKC = D / 32;
+  static constexpr int BLKP = NT * 16;  // staged rows per block, a multiple of 32
+  static constexpr int NCC = BLKP / 32;
+  // phase A: RG row-tile pairs x CG column groups
+  static constexpr int RG = NT / 2;
+  static constexpr int CG0 = kWaves / RG;
+  static constexpr int CG = CG0 < NJ ? CG0 : NJ;
+  static constexpr int NJC = NJ / CG;
+  static constexpr int AWAVES = RG * CG;
+  // phase B: PBR x PBC grid of waves over the state tiles
+  static constexpr int PBR = kWaves < 4 ? kWaves : 4;
+  static constexpr int PBC = kWaves / PBR;
+  static constexpr int BIT = NI / PBR;
+  static constexpr int BJT = NJ / PBC;
+  // direct loads: 512 elements (1 KiB) per wave instruction
+  static constexpr int KRPI = 512 / D;
+  static constexpr int VRPI = 512 / DV;
+  static constexpr int KINST = BLKP / KRPI;
+  static constexpr int VINST = BLKP / VRPI;
+  // Every wave issues the same number of direct loads per block (slots past
+  // KINST / VINST load nothing and write zeros into rows past BLKP), so the
+  // number of loads in flight is a compile-time constant.
+  static constexpr int KI_W = (KINST + kWaves - 1) / kWaves;
+  static constexpr int VI_W = (VINST + kWaves - 1) / kWaves;
+  static constexpr int N_DMA = KI_W + VI_W;
+  static_assert(KI_W * kWaves * KRPI <= kBlkMax && VI_W * kWaves * VRPI <= kBlkMax, "padding slots stay in the tile");
+  static_assert(N_DMA <= 16, "vmcnt immediate");
+  // Vector-memory issue slots of phase A: the NKC inter-block steps and the
+  // first NCH_MIN key chunks (every row-tile pair has at least that many).
+  static constexpr int NCH_MIN = (NT / 2) / 2 + 1;
+  static constexpr int NSLOT = NKC + NCH_MIN;
+  static_assert(NT % 2 == 0 && NT >= 2 && NT <= 8, "2..8 row tiles per block");
+  static_assert(NJ % CG == 0 && AWAVES <= kWaves, "phase A grid");
+  static_assert(BIT >= 1 && BJT >= 1, "phase B grid");
+  static_assert(BLKP % KRPI == 0 && BLKP % VRPI == 0, "direct-load rows");
+};
+
+template <int D, int DV, int NT, int SM>
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_bf16_kernel(PrefillArgs a) {
+  using P = Plan<D, DV, NT>;
+  // Two stages of K and V tiles, and the bf16 copy of the state slice.
+  __shared__ __attribute__((aligned(1024))) u16 Ks0[kBlkMax * D];
+  __shared__ __attribute__((aligned(1024))) u16 Ks1[kBlkMax * D];
+  __shared__ __attribute__((aligned(1024))) u16 Vs0[kBlkMax * DV];
+  __shared__ __attribute__((aligned(1024))) u16 Vs1[kBlkMax * DV];
+  __shared__ __attribute__((aligned(1024))) u16 SsT[DV * D];  // SsT[j][i] = bf16(S[i][j0 + j])
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // The wave index is uniform across the wave; saying so lets every loop and
+  // branch that depends on it run on the scalar unit.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15;
+  const int g = lane >> 4;
+
+  // Workgroup -> (sequence, value slice).  With several slices per sequence
+  // and a grid that is a multiple of 8 * nsplit, the slices of one sequence
+  // get workgroup ids congruent mod 8, i.e. the same XCD (workgroups are
+  // dispatched round-robin over the 8 XCDs), so their common Q and K reads
+  // can hit that XCD's L2.
+  const int nsplit = a.nsplit;
+  int64_t bh;
+  int split;
+  const int64_t wg = blockIdx.x;
+  if (nsplit > 1 && a.xcd_map) {
+    const int64_t xcd = wg & 7, local = wg >> 3;
+    split = (int)(local % nsplit);
+    bh = (local / nsplit) * 8 + xcd;
+  } else {
+    bh = wg / nsplit;
+    split = (int)(wg % nsplit);
+  }
+  const int j0 = split * DV;
+  const int64_t N = a.N;
+  const int blk = a.blk;
+  // Block bookkeeping in 32-bit scalars (the host guarantees N / blk < 2^31).
+  const int nfull = (int)(N / blk);                       // blocks of blk tokens
+  const int last = (int)(N - (int64_t)nfull * blk);       // tokens in a final partial block
+  const int nblk = nfull + (last > 0 ? 1 : 0);
+  // state snapshots per sequence
+  const int nsnap = (SM == kPsF32Snap && a.snap) ? nfull / a.snap_every : 0;
+
+  const u16 *qh = a.q + (size_t)bh * (size_t)N * D;
+  const u16 *kh = a.k + (size_t)bh * (size_t)N * D;
+  const u16 *vh = a.v + (size_t)bh * (size_t)N * D;  // slice offset j0 added per load
+  u16 *oh = a.o + (size_t)bh * (size_t)N * D + j0;
+  const size_t st0 = (size_t)bh * D * D + j0;  // this slice of the state (elements)
+
+  constexpr int RB = D * 2;    // bytes per K row and per state-copy row
+  constexpr int VRB = DV * 2;  // bytes per V-slice row
+
+  // ---- phase B ownership: i-tiles [ib*BIT, +BIT) x j-tiles [jb*BJT, +BJT) ----
+  const int ib = wave % P::PBR, jb = wave / P::PBR;
+  // state element (x, y, e) of this lane: tile row ib*BIT+x, tile column
+  // jb*BJT+y, row 4g+e and column lr inside the tile
+  auto s_at = [&](int x, int y, int e) {
+    return st0 + (size_t)((ib * P::BIT + x) * 16 + 4 * g + e) * D + (jb * P::BJT + y) * 16 + lr;
+  };
+  // narrow formats: stored value = code * scale
+  float lp_sc = 1.f;
+  if constexpr (SM >= kPsBF16) {
+    if (a.lp_scale) lp_sc = a.lp_scale[bh];
+  }
+  const float lp_inv = 1.f / lp_sc;
+  f32x4 S_acc[P::BIT][P::BJT];
+#pragma unroll
+  for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+    for (int y = 0; y < P::BJT; ++y)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (SM == kPsBF16)
+          S_acc[x][y][e] = bf16_bits_to_f32(((const u16 *)a.lp_state)[s_at(x, y, e)]) * lp_sc;
+        else if constexpr (SM == kPsE4M3)
+          S_acc[x][y][e] = __builtin_amdgcn_cvt_f32_fp8((int)((const uint8_t *)a.lp_state)[s_at(x, y, e)], 0) * lp_sc;
+        else
+          S_acc[x][y][e] = a.state[s_at(x, y, e)];
+      }
+
+  // ---- phase A role: row tiles {rg, NT-1-rg} x value tiles [jc0, jc0 + NJC) ----
+  const bool act = P::AWAVES == kWaves || wave < P::AWAVES;
+  const int rg = wave % P::RG;
+  const int jc0 = (wave / P::RG) * P::NJC;
+
+  // ---- per-lane LDS byte offsets ----
+  // Every tile row used below is a multiple of 16 plus a lane-dependent part,
+  // and the swizzle only looks at the low 4 row bits, so each access is a
+  // per-lane part plus a compile-time row offset (an immediate).  The
+  // per-lane parts are recomputed (a few integer operations) from a lane id
+  // the compiler cannot hoist, where they are used: keeping all of them live
+  // across the block loop would cost ~40 registers the matrix pipeline needs.
+  struct LaneOff {
+    int lr, g, h, lo8, rr;
+  };
+  auto lane_off = [&]() __attribute__((always_inline)) {
+    const int ln = lane_now();
+    LaneOff o;
+    o.lr = ln & 15;
+    o.g = ln >> 4;
+    o.h = (o.lr & 3) >> 1;
+    o.lo8 = 8 * (o.lr & 1);
+    o.rr = 4 * o.g + (o.lr >> 2);  // row of a transposing read within 16
+    return o;
+  };
+  // 16-byte fragment of row lr, chunk 4kc+g (K rows and the state copy)
+  auto kfrag = [&](const LaneOff &o, int kc) { return o.lr * RB + (swz<P::CPRK>(o.lr, 4 * kc + o.g) << 4); };
+  // transposing-read operand of value tile jt (V) and key tile it (K^T)
+  auto vtr = [&](const LaneOff &o, int jt) { return o.rr * VRB + (swz<P::CPRV>(o.rr, 2 * jt + o.h) << 4) + o.lo8; };
+  auto ktr = [&](const LaneOff &o, int it) { return o.rr * RB + (swz<P::CPRK>(o.rr, 2 * it + o.h) << 4) + o.lo8; };
+
+  auto ld128 = [](const u16 *base, int off) { return *(const bf16x8 *)((const char *)base + off); };
+  auto ldtr = [](const u16 *base, int off0, int off1) {
+    return join_tr(lds_read_tr((const u16 *)((const char *)base + off0)),
+                   lds_read_tr((const u16 *)((const char *)base + off1)));
+  };
+
+  auto write_state_copy = [&]() {
+    const LaneOff lo = lane_off();
+    const int lr = lo.lr, g = lo.g;
+#pragma unroll
+    for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+      for (int y = 0; y < P::BJT; ++y) {
+        const int off = ((jb * P::BJT + y) * 16 + lr) * RB + (swz<P::CPRK>(lr, 2 * (ib * P::BIT + x) + (g >> 1)) << 4) +
+                        8 * (g & 1);
+        lds_store_b64((const char *)SsT + off, pack_bf16x4(S_acc[x][y]));
+      }
+  };
+
+  // ---- Q rows of the wave's two row tiles (registers) ----
+  bf16x8 bq[2][P::NKC], qn[2][P::NKC];
+  // Row tiles of the wave's pair: T0 = rg and T1 = NT-1-rg.  Waves without
+  // phase-A work load and store nothing through zero-size descriptors, so
+  // that every wave issues the same vector-memory operations.
+  const int T0 = rg, T1 = NT - 1 - rg;
+  auto load_q_part = [&](int64_t tok0, int len, int u, int kc) __attribute__((always_inline)) {
+    // descriptor built from scalar-forced words: with the generic builder the
+    // compiler could not prove it uniform and looped over lanes per load
+    const u32x4 dq = raw_desc(qh + (size_t)tok0 * D, act ? (uint32_t)len * D * 2 : 0u);
+    __amdgpu_buffer_rsrc_t rq;
+    __builtin_memcpy(&rq, &dq, sizeof(rq));
+    const LaneOff lo = lane_off();
+    const int qlane = (lo.lr * D + 8 * lo.g) * 2;  // Q fragment of row lr
+    qn[u][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rq, qlane, (16 * (u ? T1 : T0) * D + kc * 32) * 2, 0));
+  };
+  auto load_q = [&](int64_t tok0, int len) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kc = 0; kc < P::NKC; ++kc) load_q_part(tok0, len, u, kc);
+  };
+
+  // ---- direct HBM -> LDS loads of the K and V tiles of one block ----
+  // Rows past len (a partial last block) and the padding slots read zeros.
+  // A wave issues N_DMA such loads per block, one at a time (kv_issue), so
+  // that they can be spread over the matrix work of the previous block.
+  struct KvDma {
+    int64_t tok0;
+    int len;
+    u16 *Kd, *Vd;
+  };
+  auto kv_prepare = [&](int64_t tok0, int len, u16 *Kd, u16 *Vd) __attribute__((always_inline)) {
+    return KvDma{tok0, len, Kd, Vd};
+  };
+  // The descriptors are rebuilt for every load (a few scalar operations) so
+  // that none of them occupies scalar registers across the matrix work.
+  auto kv_issue = [&](const KvDma &d, int m) __attribute__((always_inline)) {
+    const int lane = lane_now();
+    unsigned zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    if (m < P::KI_W) {
+      const int inst = wave + kWaves * m;
+      const int row = inst * P::KRPI + lane / P::CPRK;
+      const int c = swz<P::CPRK>(row, lane % P::CPRK);
+      const u32x4 desc = raw_desc(kh + (size_t)d.tok0 * D, inst < P::KINST ? (uint32_t)d.len * D * 2 + zero : 0u);
+      dma_b128(desc, (row * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
+    } else {
+      const int inst = wave + kWaves * (m - P::KI_W);
+      const int row = inst * P::VRPI + lane / P::CPRV;
+      const int c = swz<P::CPRV>(row, lane % P::CPRV);
+      const u32x4 desc = raw_desc(vh + (size_t)d.tok0 * D, inst < P::VINST ? (uint32_t)d.len * D * 2 + zero : 0u);
+      dma_b128(desc, (row * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
+    }
+  };
+  auto kv_issue_all = [&](const KvDma &d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < P::N_DMA; ++m) kv_issue(d, m);
+  };
+  auto block_len = [&](int jb) { return jb < nfull ? blk : last; };
+
+
+  // ---- phase A for row-tile pair {RGI, NT-1-RGI}: output rows ----
+  auto phase_a = [&](auto rgi, const u16 *Kc, const u16 *Vc, f32x4 (&acc)[2][P::NJC], auto &&vm_slot)
+                     __attribute__((always_inline)) {
+
+    constexpr int T[2] = {decltype(rgi)::value, NT - 1 - decltype(rgi)::value};
+    constexpr int NCH = T[1] / 2 + 1;  // 32-key chunks this pair touches
+
+    // Operands of a 32-key chunk: K rows (A operand of P^T = K Q^T, one
+    // buffer, refilled for the next chunk as soon as this chunk's P products
+    // have been issued) and V^T (A operand of O^T += V^T P^T, two buffers).
+    auto need = [](int cc, int s, int u) constexpr { return 2 * cc + s <= T[u] && cc <= T[u] / 2; };
+    const LaneOff lo = lane_off();
+    int kf[P::NKC], vtrA[P::NJC];
+#pragma unroll
+    for (int kc = 0; kc < P::NKC; ++kc) kf[kc] = kfrag(lo, kc);
+#pragma unroll
+    for (int jl = 0; jl < P::NJC; ++jl) vtrA[jl] = vtr(lo, jc0 + jl);
+    bf16x8 kbuf[2][P::NKC];
+    bf16x8 vbuf[2][P::NJC];
+    auto load_k = [&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (!need(cc, s, 0) && !need(cc, s, 1)) continue;
+#pragma unroll
+        for (int kc = 0; kc < P::NKC; ++kc) kbuf[s][kc] = ld128(Kc, kf[kc] + (32 * cc + 16 * s) * RB);
+      }
+    };
+    auto load_v = [&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+      const int c0 = 32 * cc;
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl)
+        vbuf[cc & 1][jl] = ldtr(Vc, vtrA[jl] + c0 * VRB, vtrA[jl] + (c0 + 16) * VRB);
+    };
+
+    // inter-block part: O^T += S^T Q^T (each state operand feeds both row
+    // tiles).  The state operands of step kc + 1 are requested before the
+    // products of step kc; the first key chunk's operands during the last two.
+    bf16x8 sfr[P::NKC][P::NJC];
+    auto load_s = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) sfr[kc][jl] = ld128(SsT, kf[kc] + (jc0 + jl) * 16 * RB);
+    };
+    load_s(0);
+#pragma unroll
+    for (int kc = 0; kc < P::NKC; ++kc) {
+      vm_slot(kc);  // a share of the next block's Q rows and K/V tiles
+      if (kc + 1 < P::NKC) load_s(kc + 1);
+      if (kc == P::NKC - 2 || (P::NKC == 1 && kc == 0)) load_k(std::integral_constant<int, 0>{});
+      if (kc == P::NKC - 1) load_v(std::integral_constant<int, 0>{});
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) {
+        acc[0][jl] = mfma_16x16x32(sfr[kc][jl], bq[0][kc], acc[0][jl]);
+        acc[1][jl] = mfma_16x16x32(sfr[kc][jl], bq[1][kc], acc[1][jl]);
+      }
+    }
+
+    // intra-block part, 32 keys at a time: O^T += V^T (P ⊙ M)^T.  Chunk cc
+    // holds keys 32cc .. 32cc+31; row tile t uses chunks 0 .. t/2, and only
+    // its last chunk straddles the diagonal.
+    static_for<NCH>([&](auto ci) __attribute__((always_inline)) {
+      constexpr int cc = decltype(ci)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (cc < P::NCH_MIN) vm_slot(P::NKC + cc);
+      // pt[u][s][e] = P[16 T_u + lr][32 cc + 16 s + 4g + e]   (P^T = K Q^T)
+      f32x4 pt[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          pt[u][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (!need(cc, s, u)) continue;
+#pragma unroll
+          for (int kc = 0; kc < P::NKC; ++kc) pt[u][s] = mfma_16x16x32(kbuf[s][kc], bq[u][kc], pt[u][s]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (cc + 1 < NCH) {
+        load_k(std::integral_constant<int, cc + 1>{});
+        load_v(std::integral_constant<int, cc + 1>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (cc > T[u] / 2) continue;
+        // keys 16(2cc+s) + 4g + e against token 16 T_u + lr
+        bf16x8 pb;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int kt = 2 * cc + s;  // 16-key tile index
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bf16 val;
+            if (kt < T[u])
+              val = (bf16)pt[u][s][e];  // whole tile below the diagonal
+            else if (kt == T[u])
+              val = (4 * g + e <= lr) ? (bf16)pt[u][s][e] : (bf16)0.f;  // diagonal tile
+            else
+              val = (bf16)0.f;  // above the diagonal
+            pb[4 * s + e] = val;
+          }
+        }
+#pragma unroll
+        for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = mfma_16x16x32(vbuf[cc & 1][jl], pb, acc[u][jl]);
+      }
+    });
+
+  };
+
+  // Call f(integral_constant<int, rg>) for the wave's row-tile pair.
+  // Exactly one call on every path (the last case is unconditional), which
+  // lets the compiler count the memory operations each path issues.
+  auto with_rg = [&](auto &&f) __attribute__((always_inline)) {
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, (P::RG > 1 ? 1 : 0)>;
+    using I2 = std::integral_constant<int, (P::RG > 2 ? 2 : 0)>;
+    using I3 = std::integral_constant<int, (P::RG > 3 ? 3 : 0)>;
+    if constexpr (P::RG == 1) {
+      f(I0{});
+    } else if constexpr (P::RG == 2) {
+      if (rg == 0) f(I0{}); else f(I1{});
+    } else if constexpr (P::RG == 3) {
+      if (rg == 0) f(I0{}); else if (rg == 1) f(I1{}); else f(I2{});
+    } else {
+      if (rg == 0) f(I0{}); else if (rg == 1) f(I1{}); else if (rg == 2) f(I2{}); else f(I3{});
+    }
+  };
+
+  // ---- output rows of the wave's pair: acc[u][jl][e] =
+  // O[16 T_u + lr][(jc0 + jl) * 16 + 4g + e].  Rows past len fall outside the
+  // descriptor and are dropped, so every wave issues the same stores. ----
+  auto store_o_part = [&](int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jl)
+                          __attribute__((always_inline)) {
+    const u32x4 dod = raw_desc(oh + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
+    __amdgpu_buffer_rsrc_t ro;
+    __builtin_memcpy(&ro, &dod, sizeof(ro));
+    // The row-tile part of the offset goes in the scalar offset, so each
+    // lane needs one address register for all of these stores.
+    const LaneOff lo_st = lane_off();
+    const int olane = (lo_st.lr * D + jc0 * 16 + 4 * lo_st.g) * 2;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, packed[u][jl]), ro, olane + jl * 32,
+                                          16 * (u ? T1 : T0) * D * 2, 0);
+  };
+
+  // ---- one block.  On entry the direct loads of block jblk (into Kc, Vc)
+  // and its Q rows (issued interleaved), then the output stores of block
+  // jblk-1, may be in flight; the other stage (Kn, Vn) is free (its block's
+  // reads ended at the previous block's second barrier).  During the block
+  // the wave issues, spread over its matrix work so that no burst stalls it
+  // on a full memory queue: the Q rows and K/V tiles of block jblk+1 (in
+  // phase A) and this block's output stores (in phase B). ----
+  auto body = [&](int jblk, const u16 *Kc, const u16 *Vc, u16 *Kn, u16 *Vn) __attribute__((always_inline)) {
+    const int64_t tok0 = (int64_t)jblk * blk;
+    const int len = block_len(jblk);
+    const int nlen = jblk + 1 < nblk ? block_len(jblk + 1) : 0;
+    // Wait for this block's tiles and Q rows; the previous block's 2 NJC
+    // output stores, issued after them, may stay in flight.
+    wait_vmcnt(jblk == 0 ? 0 : 2 * P::NJC);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kc = 0; kc < P::NKC; ++kc) bq[u][kc] = qn[u][kc];
+    lds_barrier();  // every wave's tiles of block jblk and the state copy are in LDS
+
+    // the next block's loads, one share per issue slot
+    const KvDma dma = kv_prepare(tok0 + blk, nlen, Kn, Vn);
+    auto vm_slot = [&](int slot) __attribute__((always_inline)) {
+      if (slot < P::NKC) {
+        load_q_part(tok0 + blk, nlen, 0, slot);
+        load_q_part(tok0 + blk, nlen, 1, slot);
+      }
+      if (nlen > 0) {
+#pragma unroll
+        for (int m = slot * P::N_DMA / P::NSLOT; m < (slot + 1) * P::N_DMA / P::NSLOT; ++m) kv_issue(dma, m);
+      }
+    };
+
+    // ---------------- phase A: output rows ----------------
+    f32x4 acc[2][P::NJC];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (act) {
+      with_rg([&](auto rgi) { phase_a(rgi, Kc, Vc, acc, vm_slot); });
+    } else {
+#pragma unroll
+      for (int slot = 0; slot < P::NSLOT; ++slot) vm_slot(slot);
+    }
+    uint2 packed[2][P::NJC];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) packed[u][jl] = pack_bf16x4(acc[u][jl]);
+
+    // ---------------- phase B: state update S += K^T V ----------------
+    // (with this block's output stores spread over its chunks)
+    const LaneOff lob = lane_off();
+    int ktrB[P::BIT], vtrB[P::BJT];  // K^T and V operands of phase B
+#pragma unroll
+    for (int x = 0; x < P::BIT; ++x) ktrB[x] = ktr(lob, ib * P::BIT + x);
+#pragma unroll
+    for (int y = 0; y < P::BJT; ++y) vtrB[y] = vtr(lob, jb * P::BJT + y);
+#pragma unroll
+    for (int cc = 0; cc < P::NCC; ++cc) {
+      const int c0 = 32 * cc;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = cc * 2 * P::NJC / P::NCC; i < (cc + 1) * 2 * P::NJC / P::NCC; ++i)
+        store_o_part(tok0, len, packed, i / P::NJC, i % P::NJC);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 ka[P::BIT], vb[P::BJT];
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x) ka[x] = ldtr(Kc, ktrB[x] + c0 * RB, ktrB[x] + (c0 + 16) * RB);
+#pragma unroll
+      for (int y = 0; y < P::BJT; ++y) vb[y] = ldtr(Vc, vtrB[y] + c0 * VRB, vtrB[y] + (c0 + 16) * VRB);
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y) S_acc[x][y] = mfma_16x16x32(ka[x], vb[y], S_acc[x][y]);
+    }
+
+    // the carry stored in the narrow format after every block (if asked)
+    if constexpr (SM >= kPsBF16) {
+      if (a.lp_round) {
+#pragma unroll
+        for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+          for (int y = 0; y < P::BJT; ++y) S_acc[x][y] = round_to_store<SM>(S_acc[x][y], lp_sc, lp_inv);
+      }
+    }
+
+    // optional snapshot of S after this block (full blocks only)
+    if (SM == kPsF32Snap && nsnap > 0 && (jblk + 1) % a.snap_every == 0 && (jblk + 1) / a.snap_every <= nsnap) {
+      float *sp = a.snap + ((size_t)bh * nsnap + ((jblk + 1) / a.snap_every - 1)) * D * D + j0;
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sp[(size_t)((ib * P::BIT + x) * 16 + 4 * g + e) * D + (jb * P::BJT + y) * 16 + lr] = S_acc[x][y][e];
+    }
+
+    // Every wave's reads of this stage and of the state copy are complete
+    // (only LDS accesses are drained, not the loads in flight).
+    lds_barrier();
+    write_state_copy();  // bf16 copy of S_jblk for the next block's phase A
+  };
+
+  {
+    const int len0 = block_len(0);
+    kv_issue_all(kv_prepare(0, len0, Ks0, Vs0));
+    load_q(0, len0);
+    // The initial state and the first Q rows are consumed here, before the
+    // loop, so the compiler's waits for their loads stay out of the
+    // pipelined loop (where they would drain the loads in flight).
+    write_state_copy();
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kc = 0; kc < P::NKC; ++kc) asm volatile("" ::"v"(qn[u][kc]));
+  }
+  for (int jblk = 0; jblk < nblk; jblk += 2) {
+    body(jblk, Ks0, Vs0, Ks1, Vs1);
+    if (jblk + 1 < nblk) body(jblk + 1, Ks1, Vs1, Ks0, Vs0);
+  }
+
+  // ---- final state ----
+#pragma unroll
+  for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+    for (int y = 0; y < P::BJT; ++y) {
+      if constexpr (SM == kPsE4M3) {
+        const f32x4 sv = S_acc[x][y];
+        const uint32_t w = f32_to_e4m3x4(f32x4{sv[0] * lp_inv, sv[1] * lp_inv, sv[2] * lp_inv, sv[3] * lp_inv});
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ((uint8_t *)a.lp_state)[s_at(x, y, e)] = (uint8_t)(w >> (8 * e));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (SM == kPsBF16)
+            ((u16 *)a.lp_state)[s_at(x, y, e)] = f32_to_bf16_bits(S_acc[x][y][e] * lp_inv);
+          else
+            a.state[s_at(x, y, e)] = S_acc[x][y][e];
+        }
+      }
+    }
+}
+
+template <int D, int DV, int SM>
+hipError_t launch_nt(const PrefillArgs &a, int64_t BH, hipStream_t stream) {
+  const int blkp = (a.blk + 31) & ~31;
+  const dim3 grid((unsigned)(BH * a.nsplit)), block(kThreads);
+  switch (blkp) {
+    case 32: hipLaunchKernelGGL((prefill_bf16_kernel<D, DV, 2, SM>), grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((prefill_bf16_kernel<D, DV, 4, SM>), grid, block, 0, stream, a); break;
+    case 96: hipLaunchKernelGGL((prefill_bf16_kernel<D, DV, 6, SM>), grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((prefill_bf16_kernel<D, DV, 8, SM>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Launch over the (d, nsplit) variants; sets the XCD mapping.
+template <int SM>
+hipError_t prefill_bf16_dispatch(PrefillArgs a, int64_t BH, int d, hipStream_t stream) {
+  a.xcd_map = (a.nsplit > 1 && (BH * a.nsplit) % (8 * a.nsplit) == 0) ? 1 : 0;
+  if (d == 128) {
+    switch (a.nsplit) {
+      case 1: return launch_nt<128, 128, SM>(a, BH, stream);
+      case 2: return launch_nt<128, 64, SM>(a, BH, stream);
+      case 4: return launch_nt<128, 32, SM>(a, BH, stream);
+    }
+  } else if (d == 64) {
+    switch (a.nsplit) {
+      case 1: return launch_nt<64, 64, SM>(a, BH, stream);
+      case 2: return launch_nt<64, 32, SM>(a, BH, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace lal

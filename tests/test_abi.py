@@ -29,8 +29,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("lin_attn_prefill", "lin_attn_prefill_ex", "lin_attn_decode",
-              "lin_attn_prefill_recurrent", "lin_attn_state_accumulate", "lin_attn_strerror"):
+    for n in ("lin_attn_prefill", "lin_attn_prefill_ex", "lin_attn_decode", "lin_attn_decode_scaled",
+              "lin_attn_prefill_scaled", "lin_attn_prefill_recurrent", "lin_attn_state_accumulate",
+              "lin_attn_strerror"):
         assert n in names
 
 
@@ -123,6 +124,38 @@ def test_decode_validation_codes():
     for name in ("q", "k", "v", "o", "s"):
         assert dec(**{name: None}) == la.EINVAL
         assert dec(**{name: MISALIGNED}) == la.EINVAL
+
+
+def test_scaled_state_validation_codes():
+    lib = la.library()
+    SC = FAKE  # any aligned non-null address: never dereferenced by a rejected call
+
+    def dec(q=FAKE, s=FAKE, sc=SC, B=1, H=1, d=128, io=la.BF16, st=la.FP8_E4M3):
+        return lib.lin_attn_decode_scaled(q, FAKE, FAKE, FAKE, s, sc, B, H, d, io, st, None)
+
+    assert dec(B=-1) == la.EINVAL
+    assert dec(st=la.F32) == la.EUNSUPPORTED  # fp32 states are not scaled
+    assert dec(st=7) == la.EUNSUPPORTED
+    assert dec(d=32) == la.EUNSUPPORTED
+    assert dec(q=None) == la.EINVAL and dec(s=MISALIGNED) == la.EINVAL
+    assert dec(sc=FAKE + 2) == la.EINVAL  # scales are float-aligned
+    assert dec(B=0, q=None, s=None, sc=None) == la.OK
+    # the plain entry point takes an FP8 state too (unit scales)
+    assert lib.lin_attn_decode(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, la.BF16, la.FP8_E4M3, None) == la.EINVAL
+    assert lib.lin_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 96, la.BF16, la.FP8_E4M3, None) == la.EUNSUPPORTED
+
+    def pre(q=FAKE, s=FAKE, sc=SC, B=1, H=1, N=16, d=128, block=64, io=la.BF16, st=la.BF16, rc=0):
+        return lib.lin_attn_prefill_scaled(q, FAKE, FAKE, FAKE, s, sc, B, H, N, d, block, io, st, rc, None)
+
+    for kw in ({"B": -1}, {"N": -1}, {"rc": 2}, {"rc": -1}, {"q": None}, {"s": None}, {"s": MISALIGNED},
+               {"sc": FAKE + 1}):
+        assert pre(**kw) == la.EINVAL, kw
+    for kw in ({"st": la.F32}, {"st": 9}, {"io": la.F32}, {"d": 96}, {"block": 144}, {"block": 40}):
+        assert pre(**kw) == la.EUNSUPPORTED, kw
+    for st in (la.BF16, la.FP8_E4M3):
+        for rc in (0, 1):
+            assert pre(N=0, q=None, s=None, sc=None, st=st, rc=rc) == la.OK
+            assert pre(q=None, st=st, rc=rc, sc=None) == la.EINVAL  # passes every size check
 
 
 def test_recurrent_validation_codes():
