@@ -7,7 +7,8 @@ synthetic inputs already resident in HBM:
   * chunked prefill (the headline): B=4, H=64, N=32768, d=128, block 128,
     bf16 q/k/v/o, fp32 state;
   * decode, fp32 state: 256 x 64 sequences, d=128, one token;
-  * decode, bf16 state: the same, state stored in bf16;
+  * decode, bf16 state: the same, state stored in bf16; and with an OCP
+    FP8 E4M3 state under per-sequence scales;
   * token-by-token prefill and chunked prefill at B=1, H=8, N=4096, d=128,
     block 64 (the crossover comparison), run after a 512 MiB cache flush.
 
@@ -16,10 +17,15 @@ previous one left (a continuation of longer sequences), which changes no
 work.  Every kernel is timed with HIP events on the stream it runs on;
 `value` is the chunked prefill's throughput in tokens/s (B*N tokens, all
 heads) over the timed steps.  Prints ONE JSON line.
+
+``--only drift`` instead measures the rounding drift of stored states against
+the fp64 oracle along one 1M-token sequence (not part of a step; see
+drift_report).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -43,7 +49,8 @@ SHARD = dict(B=1, H=64, N=131072, d=128, block=128)
 SNAP_EVERY = 8  # blocks between prefix-cache state snapshots (every 1024 tokens)
 DRAFTS = 4      # draft tokens verified per sequence in the speculative step
 
-PREFILL_KERNEL_SOURCES = ["linear_attention_lightning_amd/csrc/prefill_bf16.hip",
+PREFILL_KERNEL_SOURCES = ["linear_attention_lightning_amd/csrc/prefill_bf16_kernel.hpp",
+                          "linear_attention_lightning_amd/csrc/prefill_bf16.hip",
                           "linear_attention_lightning_amd/csrc/common.hpp"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_B4_H64_N32768_d128_blk128_hbm_traffic.md")
 
@@ -137,7 +144,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy", "drift"],
                     help="run one kernel only (for counter collection); prints timings, no JSON")
     args = ap.parse_args()
 
@@ -157,6 +164,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.only == "drift":
+        print(json.dumps(drift_report(la, synth, torch)))
+        return
 
     if args.only == "copy":
         # plain copy of a known size, used to calibrate the HBM byte counters
@@ -185,6 +196,10 @@ def main():
     if need["decode"]:
         dS32 = synth.decode_initial_state_device(D["B"], D["H"], D["d"])
         dS16 = dS32.to(torch.bfloat16)
+        # E4M3 state under per-sequence power-of-two scales (largest stored
+        # magnitude between 112 and 224, below the format's 448)
+        dscale = torch.exp2(torch.ceil(torch.log2(dS32.abs().amax(dim=(2, 3)) / 224.0)))
+        dS8 = (dS32 / dscale[:, :, None, None]).to(torch.float8_e4m3fn)
         dq, dk, dv = synth.decode_step_inputs_device(0, D["B"], D["H"], D["d"])
         do = torch.empty_like(dq)
         # speculative step: DRAFTS drafts per sequence, verified then committed
@@ -211,7 +226,8 @@ def main():
 
     names = [n for n, on in (("prefill", need["prefill"]), ("prefill_snapshots", need["prefill"]),
                              ("decode_fp32", need["decode"]),
-                             ("decode_bf16", need["decode"]), ("verify", need["decode"]),
+                             ("decode_bf16", need["decode"]), ("decode_e4m3", need["decode"]),
+                             ("verify", need["decode"]),
                              ("commit", need["decode"]), ("small_chunked", need["small"]),
                              ("small_recurrent", need["small"]), ("shard_state_accumulate", need["shard"]),
                              ("shard_prefill", need["shard"])) if on]
@@ -230,6 +246,7 @@ def main():
         if need["decode"]:
             timed("decode_fp32", lambda: la.decode(dq, dk, dv, do, dS32))
             timed("decode_bf16", lambda: la.decode(dq, dk, dv, do, dS16))
+            timed("decode_e4m3", lambda: la.decode(dq, dk, dv, do, dS8, state_scale=dscale))
             timed("verify", lambda: la.decode_verify(tq, tk, tv, to, dS32))
             timed("commit", lambda: la.decode_commit(tk, tv, dS32, tacc))
         if need["small"]:
@@ -275,6 +292,7 @@ def main():
     traffic = measured_traffic()
     d32_bytes = decode_bytes(D["B"], D["H"], D["d"], 4)
     d16_bytes = decode_bytes(D["B"], D["H"], D["d"], 2)
+    d8_bytes = decode_bytes(D["B"], D["H"], D["d"], 1)
     small_tokens = S["B"] * S["N"]
 
     out = {
@@ -293,7 +311,7 @@ def main():
         "config": {
             "workload": "causal linear attention prefill, phi = identity, B=4 H=64 N=32768 d=128 block=128, "
                         "bf16 q/k/v/o, fp32 state",
-            "decode_workload": "256 x 64 sequences, d=128, one token per step, fp32 state and bf16 state",
+            "decode_workload": "256 x 64 sequences, d=128, one token per step, fp32, bf16 and E4M3 states",
             "crossover_workload": "B=1 H=8 N=4096 d=128 block=64: chunked vs token-by-token",
         },
         "prefill": {
@@ -316,6 +334,8 @@ def main():
             "fp32_state_pct_hbm_peak": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9 / PEAK_HBM_GBS,
             "bf16_state_ms": avg["decode_bf16"], "bf16_state_GBps": d16_bytes / (avg["decode_bf16"] / 1e3) / 1e9,
             "bf16_state_pct_hbm_peak": 100 * d16_bytes / (avg["decode_bf16"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "e4m3_state_ms": avg["decode_e4m3"], "e4m3_state_GBps": d8_bytes / (avg["decode_e4m3"] / 1e3) / 1e9,
+            "e4m3_state_pct_hbm_peak": 100 * d8_bytes / (avg["decode_e4m3"] / 1e3) / 1e9 / PEAK_HBM_GBS,
             "tokens_per_s_fp32_state": D["B"] / (avg["decode_fp32"] / 1e3),
             "speculative": {
                 "drafts": DRAFTS, "accepted": DRAFTS - 1,
@@ -355,6 +375,144 @@ def main():
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
 
+
+
+DRIFT = dict(H=4, d=128, block=128, checkpoints=(1024, 4096, 16384, 65536, 262144, 1048576))
+
+
+def drift_report(la, synth, torch):
+    """Rounding drift of a stored state along one sequence, against the fp64
+    oracle (the hazard of low-precision state storage: "ノーフリーランチ"
+    (winzheng.jp), section "推論システム統合の課題").
+
+    One sequence of 2^20 tokens (B=1, H=4, d=128; the synthetic recipe:
+    q, k ~ N(0, 1/d), v ~ N(0, 1), bf16) is processed by
+      * decode, one token per launch, with the state stored in fp32, bf16
+        and E4M3 after every token;
+      * chunked prefill (block 128) with an fp32 carry, and with the carry
+        stored in bf16 or E4M3 after every block (lin_attn_prefill_scaled,
+        round_carry = 1);
+      * chunked prefill that stores bf16 / E4M3 once, at the end
+        (round_carry = 0): one rounding, the floor of each format.
+    E4M3 states use one power-of-two scale per head, fixed for the whole
+    sequence: the smallest that maps the largest exact |S| over the sequence
+    to at most 224.  At each checkpoint N the stored state is compared with
+    the exact S_N (oracle.state_after, fp64) and the output of token N-1
+    with the oracle's recurrence: relative errors max|x - x_exact| /
+    max|x_exact|."""
+    import numpy as np
+    from oracle import oracle
+
+    H, d, blk, cps = DRIFT["H"], DRIFT["d"], DRIFT["block"], DRIFT["checkpoints"]
+    Nmax = cps[-1]
+    t0 = time.time()
+    q, k, v = synth.prefill_inputs_device(11, 1, H, Nmax, d)
+    kh = k.float().cpu().numpy()
+    vh = v.float().cpu().numpy()
+    # exact states at every checkpoint (and one block before it)
+    S_pre, S_cp = {}, {}
+    S = np.zeros((1, H, d, d))
+    last = 0
+    for N in cps:
+        S_pre[N] = oracle.state_after(kh[:, :, last:N - blk], vh[:, :, last:N - blk], S)
+        S = oracle.state_after(kh[:, :, N - blk:N], vh[:, :, N - blk:N], S_pre[N])
+        S_cp[N] = S
+        last = N
+    smax = max(float(np.abs(S_cp[N]).max()) for N in cps)
+    head_max = np.max(np.stack([np.abs(S_cp[N]).max(axis=(2, 3)) for N in cps]), axis=0)  # [1, H]
+    scale = np.exp2(np.ceil(np.log2(head_max / 224.0))).astype(np.float32)
+    o_ref = {}
+    for N in cps:
+        qb = q[:, :, N - blk:N].float().cpu().numpy()
+        o_ref[N] = oracle.recurrence(qb, kh[:, :, N - blk:N], vh[:, :, N - blk:N], S_pre[N])[0][:, :, -1]
+    print(f"[drift] exact states ready ({time.time() - t0:.1f} s)", file=sys.stderr, flush=True)
+
+    dev = q.device
+    scd = torch.from_numpy(scale).to(dev)
+    fmts = {"bf16": (torch.bfloat16, oracle.FMT_BF16), "e4m3": (torch.float8_e4m3fn, oracle.FMT_E4M3)}
+
+    def widen(t, fmt):
+        if fmt == "fp32":
+            return t.double().cpu().numpy()
+        codes = t.cpu().view(torch.int16 if fmt == "bf16" else torch.uint8).numpy()
+        if fmt == "bf16":
+            codes = codes.view(np.uint16)
+        return oracle.stored_to_f64(codes, fmts[fmt][1], scale if fmt == "e4m3" else None)
+
+    def err(x, ref):
+        return float(np.max(np.abs(x - ref)) / np.max(np.abs(ref)))
+
+    rows = {N: {"N": N, "state": {}, "output": {}} for N in cps}
+    o = torch.empty_like(q)
+    # chunked prefill, chained over the checkpoints (a continuation; with the
+    # carry rounded every block this is the same computation as one call)
+    for name, fmt, rc in (("prefill_fp32_carry", "fp32", None), ("prefill_bf16_carry", "bf16", True),
+                          ("prefill_e4m3_carry", "e4m3", True)):
+        st = torch.zeros((1, H, d, d), dtype=torch.float32, device=dev)
+        if fmt != "fp32":
+            st = st.to(fmts[fmt][0])
+        last = 0
+        for N in cps:
+            sl = slice(last, N)
+            seg = [t[:, :, sl].contiguous() for t in (q, k, v)]
+            os_ = torch.empty_like(seg[0])
+            if fmt == "fp32":
+                la.prefill(*seg, os_, st, blk)
+            else:
+                la.prefill_scaled(*seg, os_, st, blk, state_scale=scd if fmt == "e4m3" else None, round_carry=rc)
+            torch.cuda.synchronize()
+            rows[N]["state"][name] = err(widen(st, fmt), S_cp[N])
+            rows[N]["output"][name] = err(os_[:, :, -1].float().cpu().numpy(), o_ref[N])
+            last = N
+    # one rounding at the end
+    for name, fmt in (("prefill_bf16_once", "bf16"), ("prefill_e4m3_once", "e4m3")):
+        for N in cps:
+            st = torch.zeros((1, H, d, d), dtype=fmts[fmt][0], device=dev)
+            la.prefill_scaled(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(), v[:, :, :N].contiguous(),
+                              o[:, :, :N].contiguous(), st, blk, state_scale=scd if fmt == "e4m3" else None,
+                              round_carry=False)
+            torch.cuda.synchronize()
+            rows[N]["state"][name] = err(widen(st, fmt), S_cp[N])
+    print(f"[drift] prefill paths done ({time.time() - t0:.1f} s)", file=sys.stderr, flush=True)
+    # decode: token-major copies so each token's [1, H, d] slice is contiguous;
+    # the C entry points are called directly with per-token pointers
+    qt, kt, vt = (t.permute(2, 0, 1, 3).contiguous() for t in (q, k, v))
+    lib = la.library()
+    step = H * d * 2
+    states = {"fp32": torch.zeros((1, H, d, d), dtype=torch.float32, device=dev),
+              "bf16": torch.zeros((1, H, d, d), dtype=torch.bfloat16, device=dev),
+              "e4m3": torch.zeros((1, H, d, d), dtype=torch.float8_e4m3fn, device=dev)}
+    outs = {f: torch.empty((1, H, d), dtype=torch.bfloat16, device=dev) for f in states}
+    code = {"fp32": la.F32, "bf16": la.BF16, "e4m3": la.FP8_E4M3}
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    qp, kp, vp = qt.data_ptr(), kt.data_ptr(), vt.data_ptr()
+    sp = {f: states[f].data_ptr() for f in states}
+    op = {f: outs[f].data_ptr() for f in states}
+    scp = scd.data_ptr()
+    t_done = 0
+    for N in cps:
+        for t in range(t_done, N):
+            off = t * step
+            for f in ("fp32", "bf16", "e4m3"):
+                rc = lib.lin_attn_decode_scaled(qp + off, kp + off, vp + off, op[f], sp[f], scp, 1, H, d, la.BF16,
+                                                code[f], stream) if f == "e4m3" else \
+                    lib.lin_attn_decode(qp + off, kp + off, vp + off, op[f], sp[f], 1, H, d, la.BF16, code[f], stream)
+                if rc != 0:
+                    raise la.LinAttnError(rc, "decode in drift_report")
+        torch.cuda.synchronize()
+        t_done = N
+        for f in states:
+            rows[N]["state"][f"decode_{f}"] = err(widen(states[f], f), S_cp[N])
+            rows[N]["output"][f"decode_{f}"] = err(outs[f].float().cpu().numpy(), o_ref[N])
+        print(f"[drift] decode reached N={N} ({time.time() - t0:.1f} s)", file=sys.stderr, flush=True)
+    return {
+        "metric": "stored-state drift vs sequence length (relative max error vs fp64 oracle)",
+        "config": {"workload": f"B=1 H={H} N up to {Nmax} d={d}, bf16 q/k/v, prefill block {blk}",
+                   "e4m3_scale_per_head": scale.reshape(-1).tolist(), "max_abs_state": smax},
+        "data": "synthetic",
+        "rows": [rows[N] for N in cps],
+        "seconds": time.time() - t0,
+    }
 
 if __name__ == "__main__":
     main()

@@ -295,3 +295,16 @@ def recurrence_stored_state(q, k, v, codes, fmt: int, scale=None, block: int = 1
     if rc != 0:
         raise RuntimeError(f"oracle stored-state recurrence failed with code {rc}")
     return o
+
+
+def state_after(k, v, S0=None) -> np.ndarray:
+    """The recurrence's state after the tokens of k, v: S_N = S_0 + sum_t
+    k_t v_t^T, in float64, as one matrix product K^T V per head (the sum the
+    recurrence accumulates, without the outputs; for long sequences whose
+    outputs are not needed).  k, v: [..., N, d]; S0: [..., d, d] or None."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    S = np.matmul(np.swapaxes(k, -1, -2), v)
+    if S0 is not None:
+        S = S + np.asarray(S0, dtype=np.float64)
+    return S

@@ -205,6 +205,23 @@ def test_linearity():
     assert rel_err(o_sum, o1 + o_q2) < 1e-12
 
 
+def test_state_after_is_the_recurrence_state():
+    """The matrix-product form of the final state agrees with the token loop:
+    exactly on integers, to fp64 rounding on random values, and it splits at
+    any point (continuation)."""
+    q, k, v = (x.astype(np.float32) for x in np.random.default_rng(41).integers(-3, 4, (3, 2, 3, 50, 8)))
+    S0 = np.random.default_rng(42).integers(-5, 6, (2, 3, 8, 8)).astype(np.float64)
+    _, S_ref = oracle.recurrence(q, k, v, S0)
+    np.testing.assert_array_equal(oracle.state_after(k, v, S0), S_ref)
+    q, k, v, S0 = rand_case(43, (2,), 300, 16)
+    _, S_ref = oracle.recurrence(q, k, v, S0)
+    S = oracle.state_after(k, v, S0)
+    assert np.max(np.abs(S - S_ref)) <= 1e-12 * np.max(np.abs(S_ref))
+    S_split = oracle.state_after(k[:, 120:], v[:, 120:], oracle.state_after(k[:, :120], v[:, :120], S0))
+    assert np.max(np.abs(S_split - S_ref)) <= 1e-12 * np.max(np.abs(S_ref))
+    assert np.array_equal(oracle.state_after(k[:, :0], v[:, :0], S0), S0)
+
+
 def test_empty_inputs():
     q = np.zeros((2, 0, 4), np.float32)
     S0 = np.ones((2, 4, 4))
