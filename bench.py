@@ -18,6 +18,8 @@ work.  Every kernel is timed with HIP events on the stream it runs on;
 `value` is the chunked prefill's throughput in tokens/s (B*N tokens, all
 heads) over the timed steps.  Prints ONE JSON line.
 
+``--only crossover`` sweeps the chunked and the token-by-token prefill over
+N = 256 ... 32768 at the crossover shape (see crossover_sweep).
 ``--only drift`` instead measures the rounding drift of stored states against
 the fp64 oracle along one 1M-token sequence (not part of a step; see
 drift_report).
@@ -144,7 +146,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy", "drift"],
+    ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy", "drift", "crossover"],
                     help="run one kernel only (for counter collection); prints timings, no JSON")
     args = ap.parse_args()
 
@@ -167,6 +169,9 @@ def main():
 
     if args.only == "drift":
         print(json.dumps(drift_report(la, synth, torch)))
+        return
+    if args.only == "crossover":
+        print(json.dumps(crossover_sweep(la, synth, torch, steps=args.steps)))
         return
 
     if args.only == "copy":
@@ -375,6 +380,57 @@ def main():
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
 
+
+
+CROSSOVER = dict(B=1, Hs=(8, 256), d=128, block=64, Ns=(256, 512, 1024, 2048, 4096, 8192, 16384, 32768))
+
+
+def crossover_sweep(la, synth, torch, steps: int = 20):
+    """Chunked ("Lightning") prefill against the token-by-token recurrence
+    over sequence length, at B=1 d=128 block 64 with 8 heads (the crossover
+    shape; its 32 workgroups leave most of the GPU idle) and with 256 heads
+    (a full GPU): where does the tiled form start to pay ("ノーフリーランチ"
+    (winzheng.jp), section "計算とメモリのボトルネックの不整合": a
+    break-even of a few thousand tokens)?  Each launch follows a 512 MiB
+    write that evicts the last-level cache; times are HIP-event averages
+    over `steps` launches.  A modeled line gives causal softmax attention at
+    the bf16 matrix peak, 2 N^2 d flop per head (not built; context only).
+    """
+    B, d, blk = CROSSOVER["B"], CROSSOVER["d"], CROSSOVER["block"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    rows = []
+    for H, N in ((H, N) for H in CROSSOVER["Hs"] for N in CROSSOVER["Ns"]):
+        q, k, v = synth.prefill_inputs_device(12, B, H, N, d)
+        o = torch.empty_like(q)
+        S = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+        res = {}
+        for name, fn in (("chunked", lambda: la.prefill(q, k, v, o, S, blk)),
+                         ("recurrent", lambda: la.prefill_recurrent(q, k, v, o, S))):
+            ms = []
+            for i in range(steps + 2):
+                flush.fill_(i & 1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if i >= 2:
+                    ms.append(e0.elapsed_time(e1))
+            res[name] = sum(ms) / len(ms)
+        softmax_ms = 2.0 * N * N * d * B * H / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+        rows.append({"H": H, "N": N, "chunked_ms": res["chunked"], "recurrent_ms": res["recurrent"],
+                     "recurrent_over_chunked": res["recurrent"] / res["chunked"],
+                     "chunked_tokens_per_s": B * N / (res["chunked"] / 1e3),
+                     "recurrent_tokens_per_s": B * N / (res["recurrent"] / 1e3),
+                     "modeled_softmax_at_bf16_peak_ms": softmax_ms})
+        print(f"[crossover] H={H} N={N}: chunked {res['chunked']:.4f} ms, recurrent {res['recurrent']:.4f} ms",
+              file=sys.stderr, flush=True)
+    return {"metric": "chunked vs token-by-token prefill time over N (ms per launch)",
+            "config": {"workload": f"B={B} H in {list(CROSSOVER['Hs'])} d={d} block {blk}, "
+                                   "bf16 q/k/v/o, fp32 state, cold cache"},
+            "data": "synthetic", "steps": steps, "rows": rows}
 
 
 DRIFT = dict(H=4, d=128, block=128, checkpoints=(1024, 4096, 16384, 65536, 262144, 1048576))
