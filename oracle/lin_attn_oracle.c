@@ -362,3 +362,118 @@ void lao_round_e4m3(const double *x, uint8_t *out, int64_t n) {
 void lao_widen_e4m3(const uint8_t *c, double *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = e4m3_to_double(c[i]);
 }
+
+/* ---------------------------------------------------------------------- */
+/* Gradients of the recurrence (training), per head.                       */
+/* ---------------------------------------------------------------------- */
+/* For the scalar L = sum_t <o_t, do_t> + <S_N, dS_N>, with o_t = q_t^T S_t
+ * and S_t = S_{t-1} + k_t v_t^T ([ZENN], section "線形アテンションの数学的
+ * 基礎", recurrence equations), the chain rule through the recurrence gives:
+ *   dq_t = S_t do_t                        (S_t: the forward state at t)
+ *   G_t  = dS_N + sum_{r >= t} q_r do_r^T  (gradient reaching S_t)
+ *   dk_t = G_t v_t,   dv_t = G_t^T k_t,   dS_0 = G_0.
+ * The forward loop recomputes S_t; the backward loop carries G from the end.
+ * q, k, v, dout : [N][d] float32 ; dS_N : [d][d] double or NULL (zero) ;
+ * dq, dk, dv : [N][d] double (out) ; dS0 : [d][d] double (out) ;
+ * S : [d][d] double (in: S_0; clobbered) ; work : [d][d] double scratch. */
+static void backward_one_head(const float *q, const float *k, const float *v,
+                              const float *dout, const double *dSN, double *dq,
+                              double *dk, double *dv, double *dS0, double *S,
+                              int64_t N, int64_t d) {
+  for (int64_t t = 0; t < N; ++t) {
+    const float *kt = k + t * d, *vt = v + t * d, *dot = dout + t * d;
+    for (int64_t i = 0; i < d; ++i) {
+      const double ki = (double)kt[i];
+      for (int64_t j = 0; j < d; ++j) S[i * d + j] += ki * (double)vt[j];
+    }
+    for (int64_t i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < d; ++j) acc += S[i * d + j] * (double)dot[j];
+      dq[t * d + i] = acc;
+    }
+  }
+  double *G = dS0; /* carried in place: ends as G_0 = dS_0 */
+  for (int64_t i = 0; i < d * d; ++i) G[i] = dSN ? dSN[i] : 0.0;
+  for (int64_t t = N - 1; t >= 0; --t) {
+    const float *qt = q + t * d, *kt = k + t * d, *vt = v + t * d, *dot = dout + t * d;
+    for (int64_t i = 0; i < d; ++i) {
+      const double qi = (double)qt[i];
+      for (int64_t j = 0; j < d; ++j) G[i * d + j] += qi * (double)dot[j];
+    }
+    for (int64_t i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < d; ++j) acc += G[i * d + j] * (double)vt[j];
+      dk[t * d + i] = acc;
+    }
+    for (int64_t j = 0; j < d; ++j) dv[t * d + j] = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      const double ki = (double)kt[i];
+      for (int64_t j = 0; j < d; ++j) dv[t * d + j] += G[i * d + j] * ki;
+    }
+  }
+}
+
+typedef struct {
+  const float *q, *k, *v, *dout;
+  const double *S0, *dSN;
+  double *dq, *dk, *dv, *dS0;
+  int64_t nheads, N, d;
+  int64_t next_head;
+  pthread_mutex_t mu;
+} bwd_job_t;
+
+static void *bwd_worker(void *arg) {
+  bwd_job_t *jb = (bwd_job_t *)arg;
+  const int64_t dd = jb->d * jb->d, td = jb->N * jb->d;
+  double *S = (double *)malloc(sizeof(double) * (size_t)dd);
+  if (!S) return (void *)1;
+  for (;;) {
+    pthread_mutex_lock(&jb->mu);
+    int64_t h = jb->next_head++;
+    pthread_mutex_unlock(&jb->mu);
+    if (h >= jb->nheads) break;
+    for (int64_t i = 0; i < dd; ++i) S[i] = jb->S0 ? jb->S0[h * dd + i] : 0.0;
+    backward_one_head(jb->q + h * td, jb->k + h * td, jb->v + h * td, jb->dout + h * td,
+                      jb->dSN ? jb->dSN + h * dd : NULL, jb->dq + h * td, jb->dk + h * td,
+                      jb->dv + h * td, jb->dS0 + h * dd, S, jb->N, jb->d);
+  }
+  free(S);
+  return NULL;
+}
+
+/* Gradients of L = sum <o, dout> + <S_N, dS_N> for `nheads` heads.
+ * q, k, v, dout : [nheads][N][d] float32 ; S0, dSN : [nheads][d][d] double
+ * or NULL (zero) ; dq, dk, dv : [nheads][N][d] double (out) ;
+ * dS0 : [nheads][d][d] double (out). */
+int lao_backward(const float *q, const float *k, const float *v, const float *dout,
+                 const double *S0, const double *dSN, double *dq, double *dk, double *dv,
+                 double *dS0, int64_t nheads, int64_t N, int64_t d, int nthreads) {
+  if (nheads < 0 || N < 0 || d <= 0) return LAO_EINVAL;
+  if (nheads == 0) return LAO_OK;
+  if (!dS0 || (N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))) return LAO_EINVAL;
+  bwd_job_t jb;
+  memset(&jb, 0, sizeof jb);
+  jb.q = q; jb.k = k; jb.v = v; jb.dout = dout; jb.S0 = S0; jb.dSN = dSN;
+  jb.dq = dq; jb.dk = dk; jb.dv = dv; jb.dS0 = dS0;
+  jb.nheads = nheads; jb.N = N; jb.d = d;
+  pthread_mutex_init(&jb.mu, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > nheads) nthreads = (int)nheads;
+  int rc = LAO_OK;
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  int started = 0;
+  if (th)
+    for (int i = 0; i < nthreads; ++i) {
+      if (pthread_create(&th[i], NULL, bwd_worker, &jb) != 0) break;
+      ++started;
+    }
+  if (started == 0 && bwd_worker(&jb) != NULL) rc = LAO_ENOMEM;
+  for (int i = 0; i < started; ++i) {
+    void *ret = NULL;
+    pthread_join(th[i], &ret);
+    if (ret != NULL) rc = LAO_ENOMEM;
+  }
+  free(th);
+  pthread_mutex_destroy(&jb.mu);
+  return rc;
+}

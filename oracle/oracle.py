@@ -63,6 +63,8 @@ def _bind(path: str):
     lib.lao_round_e4m3.restype = None
     lib.lao_widen_e4m3.argtypes = [p, p, i64]
     lib.lao_widen_e4m3.restype = None
+    lib.lao_backward.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, ctypes.c_int]
+    lib.lao_backward.restype = ctypes.c_int
     return lib
 
 
@@ -107,6 +109,10 @@ def compile_variant(src_text: str, out_path: str):
         @staticmethod
         def stored_to_f64(codes, fmt, scale=None):
             return stored_to_f64(codes, fmt, scale, _lib_obj=lib)
+
+        @staticmethod
+        def backward(q, k, v, dout, S0=None, dSN=None, nthreads=None):
+            return backward(q, k, v, dout, S0, dSN, nthreads, _lib_obj=lib)
 
         @staticmethod
         def recurrence_stored_state(q, k, v, codes, fmt, scale=None, block=1, nthreads=None):
@@ -308,3 +314,41 @@ def state_after(k, v, S0=None) -> np.ndarray:
     if S0 is not None:
         S = S + np.asarray(S0, dtype=np.float64)
     return S
+
+
+def backward(q, k, v, dout, S0=None, dSN=None, nthreads: int | None = None, _lib_obj=None):
+    """Gradients of L = sum_t <o_t, dout_t> + <S_N, dSN> through the
+    recurrence: returns (dq, dk, dv, dS0) as float64 arrays.
+
+    q, k, v, dout: [..., N, d] (fp32 or bf16-valued fp32); S0, dSN:
+    [..., d, d] or None (zero)."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    *lead, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have shape {q.shape}; got {t.shape}")
+
+    def st(x):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        if x.shape != (*lead, d, d):
+            raise ValueError(f"states must have shape {(*lead, d, d)}; got {x.shape}")
+        return x
+
+    S0, dSN = st(S0), st(dSN)
+    nheads = int(np.prod(lead)) if lead else 1
+    dq = np.empty((*lead, N, d))
+    dk = np.empty((*lead, N, d))
+    dv = np.empty((*lead, N, d))
+    dS0 = np.empty((*lead, d, d))
+    if nheads == 0:
+        return dq, dk, dv, dS0
+    rc = (_lib_obj or _load()).lao_backward(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                            None if S0 is None else S0.ctypes.data,
+                                            None if dSN is None else dSN.ctypes.data,
+                                            dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, dS0.ctypes.data,
+                                            nheads, N, d, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle backward failed with code {rc}")
+    return dq, dk, dv, dS0
