@@ -383,8 +383,8 @@ static void backward_one_head(const float *q, const float *k, const float *v,
   for (int64_t t = 0; t < N; ++t) {
     const float *kt = k + t * d, *vt = v + t * d, *dot = dout + t * d;
     for (int64_t i = 0; i < d; ++i) {
-      const double ki = (double)kt[i];
-      for (int64_t j = 0; j < d; ++j) S[i * d + j] += ki * (double)vt[j];
+      const double kfi = (double)kt[i];
+      for (int64_t j = 0; j < d; ++j) S[i * d + j] += kfi * (double)vt[j];
     }
     for (int64_t i = 0; i < d; ++i) {
       double acc = 0.0;
@@ -397,8 +397,8 @@ static void backward_one_head(const float *q, const float *k, const float *v,
   for (int64_t t = N - 1; t >= 0; --t) {
     const float *qt = q + t * d, *kt = k + t * d, *vt = v + t * d, *dot = dout + t * d;
     for (int64_t i = 0; i < d; ++i) {
-      const double qi = (double)qt[i];
-      for (int64_t j = 0; j < d; ++j) G[i * d + j] += qi * (double)dot[j];
+      const double qri = (double)qt[i];
+      for (int64_t j = 0; j < d; ++j) G[i * d + j] += qri * (double)dot[j];
     }
     for (int64_t i = 0; i < d; ++i) {
       double acc = 0.0;
@@ -407,8 +407,8 @@ static void backward_one_head(const float *q, const float *k, const float *v,
     }
     for (int64_t j = 0; j < d; ++j) dv[t * d + j] = 0.0;
     for (int64_t i = 0; i < d; ++i) {
-      const double ki = (double)kt[i];
-      for (int64_t j = 0; j < d; ++j) dv[t * d + j] += G[i * d + j] * ki;
+      const double kbi = (double)kt[i];
+      for (int64_t j = 0; j < d; ++j) dv[t * d + j] += G[i * d + j] * kbi;
     }
   }
 }

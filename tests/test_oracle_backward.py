@@ -120,14 +120,14 @@ def test_backward_pin(pin):
 BWD_MUTANTS = {
     # G updated after the token's own dk, dv (the exclusive reverse sum)
     "exclusive_reverse_carry": (
-        "    for (int64_t i = 0; i < d; ++i) {\n      const double qi = (double)qt[i];\n      for (int64_t j = 0; j < d; ++j) G[i * d + j] += qi * (double)dot[j];\n    }\n    for (int64_t i = 0; i < d; ++i) {\n      double acc = 0.0;\n      for (int64_t j = 0; j < d; ++j) acc += G[i * d + j] * (double)vt[j];\n      dk[t * d + i] = acc;\n    }\n",
-        "    for (int64_t i = 0; i < d; ++i) {\n      double acc = 0.0;\n      for (int64_t j = 0; j < d; ++j) acc += G[i * d + j] * (double)vt[j];\n      dk[t * d + i] = acc;\n    }\n    for (int64_t i = 0; i < d; ++i) {\n      const double qi = (double)qt[i];\n      for (int64_t j = 0; j < d; ++j) G[i * d + j] += qi * (double)dot[j];\n    }\n"),
+        "    for (int64_t i = 0; i < d; ++i) {\n      const double qri = (double)qt[i];\n      for (int64_t j = 0; j < d; ++j) G[i * d + j] += qri * (double)dot[j];\n    }\n    for (int64_t i = 0; i < d; ++i) {\n      double acc = 0.0;\n      for (int64_t j = 0; j < d; ++j) acc += G[i * d + j] * (double)vt[j];\n      dk[t * d + i] = acc;\n    }\n",
+        "    for (int64_t i = 0; i < d; ++i) {\n      double acc = 0.0;\n      for (int64_t j = 0; j < d; ++j) acc += G[i * d + j] * (double)vt[j];\n      dk[t * d + i] = acc;\n    }\n    for (int64_t i = 0; i < d; ++i) {\n      const double qri = (double)qt[i];\n      for (int64_t j = 0; j < d; ++j) G[i * d + j] += qri * (double)dot[j];\n    }\n"),
     "dk_with_transposed_carry": ("for (int64_t j = 0; j < d; ++j) acc += G[i * d + j] * (double)vt[j];",
                                  "for (int64_t j = 0; j < d; ++j) acc += G[j * d + i] * (double)vt[j];"),
     "dq_from_transposed_state": ("for (int64_t j = 0; j < d; ++j) acc += S[i * d + j] * (double)dot[j];",
                                  "for (int64_t j = 0; j < d; ++j) acc += S[j * d + i] * (double)dot[j];"),
-    "dv_weights_from_v": ("const double ki = (double)kt[i];\n      for (int64_t j = 0; j < d; ++j) dv[t * d + j] += G[i * d + j] * ki;",
-                          "const double ki = (double)vt[i];\n      for (int64_t j = 0; j < d; ++j) dv[t * d + j] += G[i * d + j] * ki;"),
+    "dv_weights_from_v": ("const double kbi = (double)kt[i];\n      for (int64_t j = 0; j < d; ++j) dv[t * d + j] += G[i * d + j] * kbi;",
+                          "const double kbi = (double)vt[i];\n      for (int64_t j = 0; j < d; ++j) dv[t * d + j] += G[i * d + j] * kbi;"),
     "final_state_gradient_dropped": ("for (int64_t i = 0; i < d * d; ++i) G[i] = dSN ? dSN[i] : 0.0;",
                                      "for (int64_t i = 0; i < d * d; ++i) G[i] = 0.0;"),
     "initial_state_dropped": ("for (int64_t i = 0; i < dd; ++i) S[i] = jb->S0 ? jb->S0[h * dd + i] : 0.0;",
