@@ -7,6 +7,7 @@ synthetic inputs already resident in HBM:
   * chunked prefill (the headline): B=4, H=64, N=32768, d=128, block 128,
     bf16 q/k/v/o, fp32 state;
   * decode, fp32 state: 256 x 64 sequences, d=128, one token;
+  * backward (gradients of the prefill) at the prefill's shape;
   * decode, bf16 state: the same, state stored in bf16; and with an OCP
     FP8 E4M3 state under per-sequence scales;
   * token-by-token prefill and chunked prefill at B=1, H=8, N=4096, d=128,
@@ -73,6 +74,19 @@ def prefill_flops(B, H, N, d, block, **_):
 def prefill_dense_flops(B, H, N, d, block, **_):
     """Flop as the matrix cores execute them (full masked tiles)."""
     return B * H * N * (4 * d * d + 4 * d * block)
+
+
+def backward_bytes(B, H, N, d, **_):
+    """Least HBM bytes of the gradients: bf16 q, k, v, dO read once and dq,
+    dk, dv written once (14 d bytes per token-head), plus the fp32 gradient
+    of S_0 written (4 d^2 per head; no S_0 and no final-state gradient)."""
+    return B * H * (N * 14 * d + 4 * d * d)
+
+
+def backward_design_bytes(B, H, N, d, **_):
+    """Bytes the three passes move: each reads three bf16 inputs and writes
+    one bf16 output (24 d per token-head), plus the fp32 gradient of S_0."""
+    return B * H * (N * 24 * d + 4 * d * d)
 
 
 def state_accumulate_bytes(B, H, N, d, **_):
@@ -198,6 +212,10 @@ def main():
         pS2 = torch.zeros_like(pS)
         psnap = torch.empty((P["B"], P["H"], la.snapshot_count(P["N"], P["block"], SNAP_EVERY), P["d"], P["d"]),
                             dtype=torch.float32, device=dev)
+        # backward: upstream gradients of the outputs, gradients written
+        pdo = synth.prefill_inputs_device(5, P["B"], P["H"], P["N"], P["d"])[2]
+        pdq, pdk, pdv = (torch.empty_like(pq) for _ in range(3))
+        pdS0 = torch.empty_like(pS)
     if need["decode"]:
         dS32 = synth.decode_initial_state_device(D["B"], D["H"], D["d"])
         dS16 = dS32.to(torch.bfloat16)
@@ -230,6 +248,7 @@ def main():
     setup_s = time.time() - t_setup
 
     names = [n for n, on in (("prefill", need["prefill"]), ("prefill_snapshots", need["prefill"]),
+                             ("backward", need["prefill"]),
                              ("decode_fp32", need["decode"]),
                              ("decode_bf16", need["decode"]), ("decode_e4m3", need["decode"]),
                              ("verify", need["decode"]),
@@ -248,6 +267,7 @@ def main():
             timed("prefill", lambda: la.prefill(pq, pk, pv, po, pS, P["block"]))
             timed("prefill_snapshots", lambda: la.prefill_snapshots(pq, pk, pv, po, pS2, psnap, P["block"],
                                                                     SNAP_EVERY))
+            timed("backward", lambda: la.backward(pq, pk, pv, pdo, pdq, pdk, pdv, P["block"], dstate0=pdS0))
         if need["decode"]:
             timed("decode_fp32", lambda: la.decode(dq, dk, dv, do, dS32))
             timed("decode_bf16", lambda: la.decode(dq, dk, dv, do, dS16))
@@ -333,6 +353,17 @@ def main():
             "with_snapshots_ms": avg["prefill_snapshots"],
             "snapshot_every_tokens": SNAP_EVERY * P["block"],
             "snapshot_bytes": psnap.numel() * 4,
+        },
+        "backward": {
+            "ms": avg["backward"],
+            "tokens_per_s": tokens / (avg["backward"] / 1e3),
+            "minimal_bytes": backward_bytes(**P),
+            "hbm_GBps_minimal_bytes": backward_bytes(**P) / (avg["backward"] / 1e3) / 1e9,
+            "design_bytes": backward_design_bytes(**P),
+            "hbm_GBps_design_bytes": backward_design_bytes(**P) / (avg["backward"] / 1e3) / 1e9,
+            "pct_hbm_peak_design_bytes": 100 * backward_design_bytes(**P) / (avg["backward"] / 1e3) / 1e9
+            / PEAK_HBM_GBS,
+            "launches": 3,
         },
         "decode": {
             "fp32_state_ms": avg["decode_fp32"], "fp32_state_GBps": d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9,

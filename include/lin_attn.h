@@ -273,6 +273,40 @@ int lin_attn_state_accumulate(const void *k, const void *v, float *state,
                               int64_t B, int64_t H, int64_t N, int64_t d,
                               lin_attn_dtype_t io_dtype, void *stream);
 
+/*
+ * Backward pass (training): the gradients of L = sum_t <o_t, dout_t> +
+ * <S_N, dstate> through the prefill above, for upstream gradients dout of
+ * the outputs and dstate of the final state.  With the gradient reaching S_t,
+ * G_t = dstate + sum_{r >= t} q_r dout_r^T (the chain rule through the
+ * recurrence of [ZENN], section "線形アテンションの数学的基礎"):
+ *
+ *     dq_t = S_t dout_t,   dk_t = G_t v_t,   dv_t = G_t^T k_t,   dstate0 = G_0.
+ *
+ * In block form these are the prefill itself in other roles: dQ is the
+ * prefill of (dout, V, K) from S_0^T, and dV and dK are prefills of
+ * (K, Q, dout) from dstate and of (V, dout, Q) from dstate^T taken over the
+ * reversed token order (suffix sums); the first of those ends in dstate0.
+ * They run as three launches on `stream`.
+ *
+ * q, k, v, dout  : [B][H][N][d] of io_dtype (read only)
+ * state0         : [B][H][d][d] fp32, the S_0 of the forward call, or NULL
+ *                  (zero); read only
+ * dstate         : [B][H][d][d] fp32 gradient of the final state, or NULL
+ *                  (zero); read only
+ * dq, dk, dv     : [B][H][N][d] of io_dtype (written)
+ * dstate0        : [B][H][d][d] fp32 gradient of S_0 (written), or NULL
+ * block          : as lin_attn_prefill
+ *
+ * No output may alias an input or another output.
+ * Supported: io_dtype BF16, d in {64, 128}, block as for bf16 in
+ * lin_attn_prefill.  The products run on bf16 matrix cores with fp32
+ * accumulation (the carried states in fp32), as in the forward kernel.
+ */
+int lin_attn_backward(const void *q, const void *k, const void *v, const void *dout,
+                      const float *state0, const float *dstate, void *dq, void *dk, void *dv,
+                      float *dstate0, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                      lin_attn_dtype_t io_dtype, void *stream);
+
 /* Static, human-readable text for a return code (never NULL). */
 const char *lin_attn_strerror(int code);
 

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     OK,
     LinAttnError,
+    backward,
     decode,
     decode_commit,
     decode_verify,
@@ -28,6 +29,6 @@ from ._binding import (  # noqa: F401
     strerror,
 )
 
-__all__ = ["prefill", "prefill_scaled", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
+__all__ = ["prefill", "prefill_scaled", "backward", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
            "prefill_snapshots", "snapshot_count", "state_accumulate", "strerror", "library", "LinAttnError",
            "F32", "BF16", "FP8_E4M3", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]

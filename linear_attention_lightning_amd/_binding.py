@@ -58,6 +58,8 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_decode_commit.restype = i32
             lib.lin_attn_state_accumulate.argtypes = [p, p, p, i64, i64, i64, i64, i32, p]
             lib.lin_attn_state_accumulate.restype = i32
+            lib.lin_attn_backward.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
+            lib.lin_attn_backward.restype = i32
             lib.lin_attn_strerror.argtypes = [i32]
             lib.lin_attn_strerror.restype = ctypes.c_char_p
             _lib = lib
@@ -295,3 +297,30 @@ def decode_commit(k, v, state, accept=None, *, stream=None):
     if rc != OK:
         raise LinAttnError(rc, "lin_attn_decode_commit")
     return state
+
+
+def backward(q, k, v, dout, dq, dk, dv, block: int, *, state0=None, dstate=None, dstate0=None, stream=None):
+    """Gradients of the chunked prefill (``lin_attn_backward``).
+
+    q, k, v, dout, dq, dk, dv: [B, H, N, d] bf16 (dq, dk, dv written);
+    state0 (the forward call's S_0), dstate (gradient of the final state)
+    and dstate0 (written: gradient of S_0): [B, H, d, d] fp32 or None."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, (B, H, N, d), q.dtype, q.device)
+    ptrs = []
+    for name, t in (("state0", state0), ("dstate", dstate), ("dstate0", dstate0)):
+        if t is None:
+            ptrs.append(None)
+        else:
+            _check(t, name, (B, H, d, d), torch.float32, q.device)
+            ptrs.append(t.data_ptr())
+    rc = library().lin_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), ptrs[0], ptrs[1],
+                                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ptrs[2], B, H, N, d, int(block),
+                                     _dtype_code(q), _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_backward")
+    return dq, dk, dv

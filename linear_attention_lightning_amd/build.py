@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "liblin_attn.so")
-SOURCES = ["lin_attn_api.hip", "prefill_bf16.hip", "prefill_bf16_scaled.hip", "prefill_f32.hip", "decode.hip", "recurrent.hip",
+SOURCES = ["lin_attn_api.hip", "prefill_bf16.hip", "prefill_bf16_scaled.hip", "prefill_bf16_grad.hip", "prefill_f32.hip", "decode.hip", "recurrent.hip",
            "state_delta.hip", "decode_multi.hip"]
 
 ARCH = "gfx950"

@@ -30,12 +30,20 @@ struct PrefillArgs {
   void *lp_state;
   const float *lp_scale;
   int lp_round;
+  // gradient passes (prefill_bf16_grad_launch; state is then unused): the
+  // initial state from g_in (transposed if g_in_t; null = zero), the final
+  // state to g_out (null = not stored)
+  const float *g_in;
+  float *g_out;
+  int g_in_t;
 };
 int prefill_bf16_max_block(int d);
 int prefill_bf16_max_split(int d);
 hipError_t prefill_bf16_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
 // state_fmt: kStBF16 or kStE4M3
 hipError_t prefill_bf16_scaled_launch(PrefillArgs a, int64_t BH, int d, int state_fmt, hipStream_t stream);
+// reverse: walk the sequence from its end (suffix sums)
+hipError_t prefill_bf16_grad_launch(PrefillArgs a, int64_t BH, int d, bool reverse, hipStream_t stream);
 
 // Chunked prefill, fp32 I/O.
 struct PrefillF32Args {

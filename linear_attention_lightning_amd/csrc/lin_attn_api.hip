@@ -134,6 +134,55 @@ int lin_attn_prefill_scaled(const void *q, const void *k, const void *v, void *o
                       (int)round_carry);
 }
 
+int lin_attn_backward(const void *q, const void *k, const void *v, const void *dout, const float *state0,
+                      const float *dstate, void *dq, void *dk, void *dv, float *dstate0, int64_t B,
+                      int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
+                      void *stream) {
+  if (B < 0 || H < 0 || N < 0 || d < 0 || block < 0) return LIN_ATTN_EINVAL;
+  if (io_dtype != LIN_ATTN_BF16 && io_dtype != LIN_ATTN_F32) return LIN_ATTN_EUNSUPPORTED;
+  if (io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;  // the bf16 matrix-core kernel only
+  if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
+  if (block < 16 || block > lal::prefill_bf16_max_block((int)d) || block % 16 != 0) return LIN_ATTN_EUNSUPPORTED;
+  int64_t BH, total;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &total) || !mul_ok(total, d, &total) || !mul_ok(BH, d * d, &total))
+    return LIN_ATTN_EINVAL;
+  if (BH == 0) return LIN_ATTN_OK;
+  if ((state0 && !ok_ptr(state0)) || (dstate && !ok_ptr(dstate)) || (dstate0 && !ok_ptr(dstate0)))
+    return LIN_ATTN_EINVAL;
+  if (N > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(dout) || !ok_ptr(dq) || !ok_ptr(dk) ||
+                !ok_ptr(dv)))
+    return LIN_ATTN_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0 && !dstate0) return LIN_ATTN_OK;
+  int cus = 0;
+  const int rc = cu_count(&cus);
+  if (rc != LIN_ATTN_OK) return rc;
+  int nsplit = 1;
+  while (nsplit < lal::prefill_bf16_max_split((int)d) && BH * nsplit < cus) nsplit *= 2;
+  if (BH * nsplit > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  if (N / block > 0x7ffffff0) return LIN_ATTN_EUNSUPPORTED;
+  using u16p = const unsigned short *;
+  lal::PrefillArgs a{};
+  a.N = N;
+  a.blk = (int)block;
+  a.nsplit = nsplit;
+  // dV: reversed prefill of (K, Q, dout) from dS_N; it ends in dS_0 (with no
+  // tokens it only copies dS_N, or zeros, into dS_0)
+  a.q = (u16p)k; a.k = (u16p)q; a.v = (u16p)dout; a.o = (unsigned short *)dv;
+  a.g_in = dstate; a.g_in_t = 0; a.g_out = dstate0;
+  hipError_t e = lal::prefill_bf16_grad_launch(a, BH, (int)d, true, s);
+  if (e != hipSuccess || N == 0) return from_hip(e);
+  // dQ: forward prefill of (dout, V, K) from S_0^T; its final state is not needed
+  a.q = (u16p)dout; a.k = (u16p)v; a.v = (u16p)k; a.o = (unsigned short *)dq;
+  a.g_in = state0; a.g_in_t = 1; a.g_out = nullptr;
+  e = lal::prefill_bf16_grad_launch(a, BH, (int)d, false, s);
+  if (e != hipSuccess) return from_hip(e);
+  // dK: reversed prefill of (V, dout, Q) from dS_N^T
+  a.q = (u16p)v; a.k = (u16p)dout; a.v = (u16p)q; a.o = (unsigned short *)dk;
+  a.g_in = dstate; a.g_in_t = 1; a.g_out = nullptr;
+  return from_hip(lal::prefill_bf16_grad_launch(a, BH, (int)d, true, s));
+}
+
 int lin_attn_prefill(const void *q, const void *k, const void *v, void *o, float *state, int64_t B,
                      int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
                      void *stream) {

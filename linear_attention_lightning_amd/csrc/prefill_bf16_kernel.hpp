@@ -42,6 +42,15 @@
 // tiles.  The number of 16-row tiles per block, NT, is a template parameter
 // so that every loop bound is a compile-time constant.
 //
+// Reversed traversal (SM = kPsGradRev) walks the blocks from the end of the
+// sequence and reads each block's rows in reverse: logical row r of a block
+// is the token len-1-r of its span in memory.  The causal mask then keeps
+// the tokens at or after each token, so the same kernel computes suffix
+// sums -- the reverse-carried state of the gradients.  Every buffer offset
+// of a row stays in the per-lane offset register; rows past the block's end
+// get negative offsets, which lie outside the buffer descriptor, so they
+// read zeros and their stores are dropped, as in forward order.
+//
 // State storage (template parameter SM).  The state that enters and leaves
 // the kernel is fp32, optionally with snapshots of it every few blocks (a
 // prefix cache), or codes of state / scale in bf16 or OCP FP8 E4M3 (a state
@@ -70,7 +79,9 @@ enum PrefillStateMode {
   kPsF32 = 0,      // fp32 state in and out
   kPsF32Snap = 1,  // fp32 state plus snapshots
   kPsBF16 = 2,     // bf16 codes of state / scale
-  kPsE4M3 = 3      // OCP FP8 E4M3 codes of state / scale
+  kPsE4M3 = 3,     // OCP FP8 E4M3 codes of state / scale
+  kPsGrad = 4,     // fp32 state from g_in (optionally transposed, null = 0) to g_out (null: none)
+  kPsGradRev = 5   // as kPsGrad, with the token order reversed (suffix sums instead of prefix sums)
 };
 
 // Round x / scale to the storage format of SM and return the stored value
@@ -289,6 +300,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int nfull = (int)(N / blk);                       // blocks of blk tokens
   const int last = (int)(N - (int64_t)nfull * blk);       // tokens in a final partial block
   const int nblk = nfull + (last > 0 ? 1 : 0);
+  constexpr bool REV = SM == kPsGradRev;
+  // first token (memory order) of the block processed at step j, of length len
+  auto blk_tok0 = [&](int j, int len) -> int64_t {
+    if constexpr (REV)
+      return len > 0 ? N - (int64_t)j * blk - len : 0;
+    else
+      return (int64_t)j * blk;
+  };
   // state snapshots per sequence
   const int nsnap = (SM == kPsF32Snap && a.snap) ? nfull / a.snap_every : 0;
 
@@ -325,6 +344,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           S_acc[x][y][e] = bf16_bits_to_f32(((const u16 *)a.lp_state)[s_at(x, y, e)]) * lp_sc;
         else if constexpr (SM == kPsE4M3)
           S_acc[x][y][e] = __builtin_amdgcn_cvt_f32_fp8((int)((const uint8_t *)a.lp_state)[s_at(x, y, e)], 0) * lp_sc;
+        else if constexpr (SM >= kPsGrad)
+          S_acc[x][y][e] = !a.g_in ? 0.f
+                           : a.g_in_t ? a.g_in[(size_t)bh * D * D +
+                                               (size_t)(j0 + (jb * P::BJT + y) * 16 + lr) * D +
+                                               (ib * P::BIT + x) * 16 + 4 * g + e]
+                                      : a.g_in[s_at(x, y, e)];
         else
           S_acc[x][y][e] = a.state[s_at(x, y, e)];
       }
@@ -392,9 +417,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     __amdgpu_buffer_rsrc_t rq;
     __builtin_memcpy(&rq, &dq, sizeof(rq));
     const LaneOff lo = lane_off();
-    const int qlane = (lo.lr * D + 8 * lo.g) * 2;  // Q fragment of row lr
-    qn[u][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rq, qlane, (16 * (u ? T1 : T0) * D + kc * 32) * 2, 0));
+    if constexpr (REV) {
+      // row 16 T + lr is token len-1-16T-lr of the span (negative: padding)
+      const int qrow = len - 1 - 16 * (u ? T1 : T0) - lo.lr;
+      qn[u][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rq, (qrow * D + 8 * lo.g) * 2, kc * 64, 0));
+    } else {
+      const int qlane = (lo.lr * D + 8 * lo.g) * 2;  // Q fragment of row lr
+      qn[u][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rq, qlane, (16 * (u ? T1 : T0) * D + kc * 32) * 2, 0));
+    }
   };
   auto load_q = [&](int64_t tok0, int len) __attribute__((always_inline)) {
 #pragma unroll
@@ -426,13 +458,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int row = inst * P::KRPI + lane / P::CPRK;
       const int c = swz<P::CPRK>(row, lane % P::CPRK);
       const u32x4 desc = raw_desc(kh + (size_t)d.tok0 * D, inst < P::KINST ? (uint32_t)d.len * D * 2 + zero : 0u);
-      dma_b128(desc, (row * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
+      const int mrow = REV ? d.len - 1 - row : row;  // row in memory order
+      dma_b128(desc, (mrow * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
     } else {
       const int inst = wave + kWaves * (m - P::KI_W);
       const int row = inst * P::VRPI + lane / P::CPRV;
       const int c = swz<P::CPRV>(row, lane % P::CPRV);
       const u32x4 desc = raw_desc(vh + (size_t)d.tok0 * D, inst < P::VINST ? (uint32_t)d.len * D * 2 + zero : 0u);
-      dma_b128(desc, (row * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
+      const int mrow = REV ? d.len - 1 - row : row;
+      dma_b128(desc, (mrow * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
     }
   };
   auto kv_issue_all = [&](const KvDma &d) __attribute__((always_inline)) {
@@ -582,9 +616,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // The row-tile part of the offset goes in the scalar offset, so each
     // lane needs one address register for all of these stores.
     const LaneOff lo_st = lane_off();
-    const int olane = (lo_st.lr * D + jc0 * 16 + 4 * lo_st.g) * 2;
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, packed[u][jl]), ro, olane + jl * 32,
-                                          16 * (u ? T1 : T0) * D * 2, 0);
+    if constexpr (REV) {
+      const int orow = len - 1 - 16 * (u ? T1 : T0) - lo_st.lr;
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, packed[u][jl]), ro,
+                                            (orow * D + jc0 * 16 + 4 * lo_st.g) * 2 + jl * 32, 0, 0);
+    } else {
+      const int olane = (lo_st.lr * D + jc0 * 16 + 4 * lo_st.g) * 2;
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, packed[u][jl]), ro, olane + jl * 32,
+                                            16 * (u ? T1 : T0) * D * 2, 0);
+    }
   };
 
   // ---- one block.  On entry the direct loads of block jblk (into Kc, Vc)
@@ -595,9 +635,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // on a full memory queue: the Q rows and K/V tiles of block jblk+1 (in
   // phase A) and this block's output stores (in phase B). ----
   auto body = [&](int jblk, const u16 *Kc, const u16 *Vc, u16 *Kn, u16 *Vn) __attribute__((always_inline)) {
-    const int64_t tok0 = (int64_t)jblk * blk;
     const int len = block_len(jblk);
     const int nlen = jblk + 1 < nblk ? block_len(jblk + 1) : 0;
+    const int64_t tok0 = blk_tok0(jblk, len);
+    const int64_t ntok0 = blk_tok0(jblk + 1, nlen);  // the next block's first token
     // Wait for this block's tiles and Q rows; the previous block's 2 NJC
     // output stores, issued after them, may stay in flight.
     wait_vmcnt(jblk == 0 ? 0 : 2 * P::NJC);
@@ -608,11 +649,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     lds_barrier();  // every wave's tiles of block jblk and the state copy are in LDS
 
     // the next block's loads, one share per issue slot
-    const KvDma dma = kv_prepare(tok0 + blk, nlen, Kn, Vn);
+    const KvDma dma = kv_prepare(ntok0, nlen, Kn, Vn);
     auto vm_slot = [&](int slot) __attribute__((always_inline)) {
       if (slot < P::NKC) {
-        load_q_part(tok0 + blk, nlen, 0, slot);
-        load_q_part(tok0 + blk, nlen, 1, slot);
+        load_q_part(ntok0, nlen, 0, slot);
+        load_q_part(ntok0, nlen, 1, slot);
       }
       if (nlen > 0) {
 #pragma unroll
@@ -695,8 +736,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
   {
     const int len0 = block_len(0);
-    kv_issue_all(kv_prepare(0, len0, Ks0, Vs0));
-    load_q(0, len0);
+    kv_issue_all(kv_prepare(blk_tok0(0, len0), len0, Ks0, Vs0));
+    load_q(blk_tok0(0, len0), len0);
     // The initial state and the first Q rows are consumed here, before the
     // loop, so the compiler's waits for their loads stay out of the
     // pipelined loop (where they would drain the loads in flight).
@@ -712,6 +753,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   }
 
   // ---- final state ----
+  // Nothing of this wave may still be in flight when it ends (with no block
+  // to process, the first block's direct loads into LDS were never awaited).
+  wait_vmcnt(0);
 #pragma unroll
   for (int x = 0; x < P::BIT; ++x)
 #pragma unroll
@@ -726,7 +770,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         for (int e = 0; e < 4; ++e) {
           if constexpr (SM == kPsBF16)
             ((u16 *)a.lp_state)[s_at(x, y, e)] = f32_to_bf16_bits(S_acc[x][y][e] * lp_inv);
-          else
+          else if constexpr (SM >= kPsGrad) {
+            if (a.g_out) a.g_out[s_at(x, y, e)] = S_acc[x][y][e];
+          } else
             a.state[s_at(x, y, e)] = S_acc[x][y][e];
         }
       }

@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("lin_attn_prefill", "lin_attn_prefill_ex", "lin_attn_decode", "lin_attn_decode_scaled",
               "lin_attn_prefill_scaled", "lin_attn_prefill_recurrent", "lin_attn_state_accumulate",
+              "lin_attn_backward",
               "lin_attn_strerror"):
         assert n in names
 
@@ -156,6 +157,21 @@ def test_scaled_state_validation_codes():
         for rc in (0, 1):
             assert pre(N=0, q=None, s=None, sc=None, st=st, rc=rc) == la.OK
             assert pre(q=None, st=st, rc=rc, sc=None) == la.EINVAL  # passes every size check
+
+
+def test_backward_validation_codes():
+    lib = la.library()
+
+    def bwd(q=FAKE, dq=FAKE, s0=None, ds=None, ds0=None, B=1, H=1, N=16, d=128, block=64, io=la.BF16):
+        return lib.lin_attn_backward(q, FAKE, FAKE, FAKE, s0, ds, dq, FAKE, FAKE, ds0, B, H, N, d, block, io, None)
+
+    for kw in ({"B": -1}, {"N": -1}, {"block": -1}, {"q": None}, {"dq": None}, {"q": MISALIGNED},
+               {"s0": MISALIGNED}, {"ds": MISALIGNED}, {"ds0": MISALIGNED}, {"B": 1 << 40, "H": 1 << 30}):
+        assert bwd(**kw) == la.EINVAL, kw
+    for kw in ({"io": la.F32}, {"io": 9}, {"d": 96}, {"block": 144}, {"block": 8}, {"block": 40}):
+        assert bwd(**kw) == la.EUNSUPPORTED, kw
+    assert bwd(B=0, q=None, dq=None) == la.OK
+    assert bwd(N=0, q=None, dq=None) == la.OK  # no tokens and no dS_0 requested: nothing to do
 
 
 def test_recurrent_validation_codes():
