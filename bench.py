@@ -193,10 +193,17 @@ def main():
         n = 1 << 30
         x = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         y = torch.empty_like(x)
+        ms = []
         for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             y.copy_(x)
-        torch.cuda.synchronize()
-        print(f"copied {n} bytes x {args.steps}")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        avg_ms = sum(ms) / len(ms)
+        print(f"copied {n} bytes x {args.steps}: avg {avg_ms:.4f} ms, {2 * n / (avg_ms / 1e3) / 1e9:.1f} GB/s "
+              f"(read + write), best {2 * n / (min(ms) / 1e3) / 1e9:.1f} GB/s")
         return
 
     P, D, S = PREFILL, DECODE, SMALL

@@ -458,15 +458,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int row = inst * P::KRPI + lane / P::CPRK;
       const int c = swz<P::CPRK>(row, lane % P::CPRK);
       const u32x4 desc = raw_desc(kh + (size_t)d.tok0 * D, inst < P::KINST ? (uint32_t)d.len * D * 2 + zero : 0u);
-      const int mrow = REV ? d.len - 1 - row : row;  // row in memory order
-      dma_b128(desc, (mrow * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
+      dma_b128(desc, ((REV ? d.len - 1 - row : row) * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
     } else {
       const int inst = wave + kWaves * (m - P::KI_W);
       const int row = inst * P::VRPI + lane / P::CPRV;
       const int c = swz<P::CPRV>(row, lane % P::CPRV);
       const u32x4 desc = raw_desc(vh + (size_t)d.tok0 * D, inst < P::VINST ? (uint32_t)d.len * D * 2 + zero : 0u);
-      const int mrow = REV ? d.len - 1 - row : row;
-      dma_b128(desc, (mrow * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
+      dma_b128(desc, ((REV ? d.len - 1 - row : row) * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
     }
   };
   auto kv_issue_all = [&](const KvDma &d) __attribute__((always_inline)) {
@@ -635,10 +633,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // on a full memory queue: the Q rows and K/V tiles of block jblk+1 (in
   // phase A) and this block's output stores (in phase B). ----
   auto body = [&](int jblk, const u16 *Kc, const u16 *Vc, u16 *Kn, u16 *Vn) __attribute__((always_inline)) {
+    // (in forward order the reversed arms fold away at compile time, leaving
+    // exactly the forward kernel's code)
+    const int64_t tok0 = REV ? blk_tok0(jblk, block_len(jblk)) : (int64_t)jblk * blk;
     const int len = block_len(jblk);
     const int nlen = jblk + 1 < nblk ? block_len(jblk + 1) : 0;
-    const int64_t tok0 = blk_tok0(jblk, len);
-    const int64_t ntok0 = blk_tok0(jblk + 1, nlen);  // the next block's first token
     // Wait for this block's tiles and Q rows; the previous block's 2 NJC
     // output stores, issued after them, may stay in flight.
     wait_vmcnt(jblk == 0 ? 0 : 2 * P::NJC);
@@ -649,11 +648,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     lds_barrier();  // every wave's tiles of block jblk and the state copy are in LDS
 
     // the next block's loads, one share per issue slot
-    const KvDma dma = kv_prepare(ntok0, nlen, Kn, Vn);
+    const KvDma dma = kv_prepare(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, Kn, Vn);
     auto vm_slot = [&](int slot) __attribute__((always_inline)) {
       if (slot < P::NKC) {
-        load_q_part(ntok0, nlen, 0, slot);
-        load_q_part(ntok0, nlen, 1, slot);
+        load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 0, slot);
+        load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 1, slot);
       }
       if (nlen > 0) {
 #pragma unroll
@@ -736,8 +735,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
   {
     const int len0 = block_len(0);
-    kv_issue_all(kv_prepare(blk_tok0(0, len0), len0, Ks0, Vs0));
-    load_q(blk_tok0(0, len0), len0);
+    kv_issue_all(kv_prepare(REV ? blk_tok0(0, len0) : 0, len0, Ks0, Vs0));
+    load_q(REV ? blk_tok0(0, len0) : 0, len0);
     // The initial state and the first Q rows are consumed here, before the
     // loop, so the compiler's waits for their loads stay out of the
     // pipelined loop (where they would drain the loads in flight).
@@ -753,9 +752,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   }
 
   // ---- final state ----
-  // Nothing of this wave may still be in flight when it ends (with no block
-  // to process, the first block's direct loads into LDS were never awaited).
-  wait_vmcnt(0);
+  // Nothing of this wave may still be in flight when it ends: a gradient pass
+  // may have no block to process, and then the first block's direct loads
+  // into LDS were never awaited.  (Forward passes always have a block, whose
+  // loads the loop awaits.)
+  if constexpr (SM >= kPsGrad) wait_vmcnt(0);
 #pragma unroll
   for (int x = 0; x < P::BIT; ++x)
 #pragma unroll
