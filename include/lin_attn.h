@@ -214,7 +214,8 @@ int lin_attn_decode_scaled(const void *q, const void *k, const void *v, void *o,
  * state      : [B][H][d][d] of state_dtype, read only
  * T          : 0 .. 16 (0 is a no-op; larger values: LIN_ATTN_EUNSUPPORTED)
  *
- * Supported: d in {64, 128}; io_dtype and state_dtype in {F32, BF16}.
+ * Supported: d in {64, 128}; io_dtype in {F32, BF16}; state_dtype in {F32,
+ * BF16, FP8_E4M3} (FP8_E4M3 with unit scales; see lin_attn_decode_verify_scaled).
  */
 int lin_attn_decode_verify(const void *q, const void *k, const void *v, void *o, const void *state,
                            int64_t B, int64_t H, int64_t T, int64_t d,
@@ -229,13 +230,31 @@ int lin_attn_decode_verify(const void *q, const void *k, const void *v, void *o,
  * accept : DEVICE pointer to int32[B], or NULL to accept all T drafts
  *
  * With an fp32 state the result is bit-identical to a_b calls of
- * lin_attn_decode (same operations in the same order); with a bf16 state the
- * update is done in fp32 and rounded once, at the store.  Errors and limits
- * as lin_attn_decode_verify.
+ * lin_attn_decode (same operations in the same order); with a bf16 or
+ * FP8_E4M3 state the update is done in fp32 and rounded once, at the store.
+ * Errors and limits as lin_attn_decode_verify.
  */
 int lin_attn_decode_commit(const void *k, const void *v, void *state, const int32_t *accept,
                            int64_t B, int64_t H, int64_t T, int64_t d,
                            lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
+
+/*
+ * lin_attn_decode_verify and lin_attn_decode_commit for a state stored in a
+ * narrow format under per-sequence scales (the storage of
+ * lin_attn_decode_scaled: entry x held as the code of x / scale[b][h]).
+ * state_scale is a DEVICE pointer to float[B][H], or NULL for 1.0.  Verify
+ * reads the widened state; commit widens, adds the accepted drafts in fp32
+ * and rounds once at the store.
+ *
+ * Supported: as the unscaled calls, with state_dtype in {BF16, FP8_E4M3}
+ * (LIN_ATTN_F32: LIN_ATTN_EUNSUPPORTED).
+ */
+int lin_attn_decode_verify_scaled(const void *q, const void *k, const void *v, void *o, const void *state,
+                                  const float *state_scale, int64_t B, int64_t H, int64_t T, int64_t d,
+                                  lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
+int lin_attn_decode_commit_scaled(const void *k, const void *v, void *state, const float *state_scale,
+                                  const int32_t *accept, int64_t B, int64_t H, int64_t T, int64_t d,
+                                  lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream);
 
 /*
  * Token-by-token prefill: the recurrence above applied one token at a time

@@ -58,6 +58,10 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_decode_commit.restype = i32
             lib.lin_attn_state_accumulate.argtypes = [p, p, p, i64, i64, i64, i64, i32, p]
             lib.lin_attn_state_accumulate.restype = i32
+            lib.lin_attn_decode_verify_scaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
+            lib.lin_attn_decode_verify_scaled.restype = i32
+            lib.lin_attn_decode_commit_scaled.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
+            lib.lin_attn_decode_commit_scaled.restype = i32
             lib.lin_attn_backward.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
             lib.lin_attn_backward.restype = i32
             lib.lin_attn_strerror.argtypes = [i32]
@@ -259,29 +263,40 @@ def prefill_snapshots(q, k, v, o, state, snapshots, block: int, every: int, *, s
     return o
 
 
-def decode_verify(q, k, v, o, state, *, stream=None):
+def decode_verify(q, k, v, o, state, *, state_scale=None, stream=None):
     """Outputs of T draft tokens per sequence from one read of the state
-    (``lin_attn_decode_verify``); the state is not modified.
+    (``lin_attn_decode_verify``, or ``lin_attn_decode_verify_scaled`` when
+    ``state_scale`` is given); the state is not modified.
 
-    q, k, v, o: [B, H, T, d] bf16 or fp32; state: [B, H, d, d] fp32 or bf16."""
+    q, k, v, o: [B, H, T, d] bf16 or fp32; state: [B, H, d, d] fp32, bf16 or
+    float8_e4m3fn; state_scale: optional float32 [B, H] on the device."""
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
     B, H, T, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         _check(t, name, (B, H, T, d), q.dtype, q.device)
     _check(state, "state", (B, H, d, d), None, q.device)
-    rc = library().lin_attn_decode_verify(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                          state.data_ptr(), B, H, T, d, _dtype_code(q), _dtype_code(state),
-                                          _stream(stream, q.device))
+    if state_scale is None:
+        rc = library().lin_attn_decode_verify(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                              state.data_ptr(), B, H, T, d, _dtype_code(q), _dtype_code(state),
+                                              _stream(stream, q.device))
+        where = "lin_attn_decode_verify"
+    else:
+        rc = library().lin_attn_decode_verify_scaled(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                     state.data_ptr(), _scale_ptr(state_scale, B, H, q.device),
+                                                     B, H, T, d, _dtype_code(q), _dtype_code(state),
+                                                     _stream(stream, q.device))
+        where = "lin_attn_decode_verify_scaled"
     if rc != OK:
-        raise LinAttnError(rc, "lin_attn_decode_verify")
+        raise LinAttnError(rc, where)
     return o
 
 
-def decode_commit(k, v, state, accept=None, *, stream=None):
+def decode_commit(k, v, state, accept=None, *, state_scale=None, stream=None):
     """state += sum over the first accept[b] drafts of k v^T
-    (``lin_attn_decode_commit``); accept: int32 [B] on the device, or None
-    for all T drafts."""
+    (``lin_attn_decode_commit``, or ``lin_attn_decode_commit_scaled`` when
+    ``state_scale`` is given); accept: int32 [B] on the device, or None for
+    all T drafts."""
     import torch
     if k.dim() != 4:
         raise ValueError("k must be [B, H, T, d]")
@@ -290,12 +305,20 @@ def decode_commit(k, v, state, accept=None, *, stream=None):
     _check(state, "state", (B, H, d, d), None, k.device)
     if accept is not None:
         _check(accept, "accept", (B,), torch.int32, k.device)
-    rc = library().lin_attn_decode_commit(k.data_ptr(), v.data_ptr(), state.data_ptr(),
-                                          accept.data_ptr() if accept is not None else None,
-                                          B, H, T, d, _dtype_code(k), _dtype_code(state),
-                                          _stream(stream, k.device))
+    acc_ptr = accept.data_ptr() if accept is not None else None
+    if state_scale is None:
+        rc = library().lin_attn_decode_commit(k.data_ptr(), v.data_ptr(), state.data_ptr(), acc_ptr,
+                                              B, H, T, d, _dtype_code(k), _dtype_code(state),
+                                              _stream(stream, k.device))
+        where = "lin_attn_decode_commit"
+    else:
+        rc = library().lin_attn_decode_commit_scaled(k.data_ptr(), v.data_ptr(), state.data_ptr(),
+                                                     _scale_ptr(state_scale, B, H, k.device), acc_ptr,
+                                                     B, H, T, d, _dtype_code(k), _dtype_code(state),
+                                                     _stream(stream, k.device))
+        where = "lin_attn_decode_commit_scaled"
     if rc != OK:
-        raise LinAttnError(rc, "lin_attn_decode_commit")
+        raise LinAttnError(rc, where)
     return state
 
 

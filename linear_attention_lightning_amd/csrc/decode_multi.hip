@@ -19,7 +19,10 @@
 //
 // commit applies, per state element, the same fused multiply-adds in the
 // same order as T one-token decode steps; with an fp32 state the result is
-// bit-identical to them.  With a bf16 state it rounds once, at the store.
+// bit-identical to them.  With a bf16 or OCP FP8 E4M3 state it rounds once,
+// at the store.  Narrow states carry a per-sequence scale and are kept in
+// stored units (state / scale) as in the one-token decode: verify multiplies
+// the state part of its outputs by the scale, commit divides v by it.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,9 +42,15 @@ __device__ __forceinline__ float ld_io(const void *p, size_t i) {
 }
 
 // 4 consecutive state entries as fp32
-template <bool ST_BF16>
+template <int ST>
 __device__ __forceinline__ void ld_state4(const void *row, int cg, float (&s)[4]) {
-  if constexpr (ST_BF16) {
+  if constexpr (ST == kStE4M3) {
+    const f32x4 w = e4m3x4_to_f32(__builtin_nontemporal_load((const uint32_t *)row + cg));
+    s[0] = w[0];
+    s[1] = w[1];
+    s[2] = w[2];
+    s[3] = w[3];
+  } else if constexpr (ST == kStBF16) {
     const u32x2 w = __builtin_nontemporal_load((const u32x2 *)row + cg);
     s[0] = __uint_as_float(w[0] << 16);
     s[1] = __uint_as_float(w[0] & 0xffff0000u);
@@ -56,9 +65,11 @@ __device__ __forceinline__ void ld_state4(const void *row, int cg, float (&s)[4]
   }
 }
 
-template <bool ST_BF16>
+template <int ST>
 __device__ __forceinline__ void st_state4(void *row, int cg, const float (&s)[4]) {
-  if constexpr (ST_BF16) {
+  if constexpr (ST == kStE4M3) {
+    __builtin_nontemporal_store(f32_to_e4m3x4(f32x4{s[0], s[1], s[2], s[3]}), (uint32_t *)row + cg);
+  } else if constexpr (ST == kStBF16) {
     const bf16x2 lo = {(bf16)s[0], (bf16)s[1]}, hi = {(bf16)s[2], (bf16)s[3]};
     const u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     __builtin_nontemporal_store(w, (u32x2 *)row + cg);
@@ -68,9 +79,9 @@ __device__ __forceinline__ void st_state4(void *row, int cg, const float (&s)[4]
   }
 }
 
-template <int D, bool IO_BF16, bool ST_BF16>
+template <int D, bool IO_BF16, int ST>
 __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
-  constexpr int ES = ST_BF16 ? 2 : 4;
+  constexpr int ES = ST == kStF32 ? 4 : ST == kStBF16 ? 2 : 1;
   constexpr int LPR = D / 4;    // lanes per state row (4 columns each)
   constexpr int RP = 64 / LPR;  // rows per wave access
   constexpr int RPL = D / RP;   // rows per lane
@@ -115,7 +126,7 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   for (int m0 = 0; m0 < RPL; m0 += U) {
     float s[U][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) ld_state4<ST_BF16>(Sh + (size_t)(rph + RP * (m0 + u)) * D * ES, cg, s[u]);
+    for (int u = 0; u < U; ++u) ld_state4<ST>(Sh + (size_t)(rph + RP * (m0 + u)) * D * ES, cg, s[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float *qi = qT + (rph + RP * (m0 + u)) * T;
@@ -137,6 +148,14 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
       if (t < T)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[t][e] += __shfl_xor(acc[t][e], off, 64);
+  if constexpr (ST != kStF32) {
+    // the state part was read in stored units
+    const float sc = a.scale ? a.scale[h] : 1.f;
+#pragma unroll
+    for (int t = 0; t < kTMax; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][e] *= sc;
+  }
   // P was written by other lanes of this wavefront: its LDS stores precede
   // the reads below in the wavefront's in-order LDS queue once drained
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -175,9 +194,9 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   }
 }
 
-template <int D, bool IO_BF16, bool ST_BF16>
+template <int D, bool IO_BF16, int ST>
 __global__ __launch_bounds__(64 * kW) void commit_kernel(DecodeMultiArgs a) {
-  constexpr int ES = ST_BF16 ? 2 : 4;
+  constexpr int ES = ST == kStF32 ? 4 : ST == kStBF16 ? 2 : 1;
   constexpr int LPR = D / 4;
   constexpr int RP = 64 / LPR;
   constexpr int RPL = D / RP;
@@ -204,17 +223,20 @@ __global__ __launch_bounds__(64 * kW) void commit_kernel(DecodeMultiArgs a) {
   if (!valid || cnt == 0) return;
 
   const int cg = lane % LPR, rph = lane / LPR;
+  // narrow states are updated in stored units: v / scale
+  const float inv = (ST != kStF32 && a.scale) ? 1.f / a.scale[h] : 1.f;
   float vr[kTMax][4];
 #pragma unroll
   for (int t = 0; t < kTMax; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vr[t][e] = t < cnt ? ld_io<IO_BF16>(a.v, ((size_t)h * T + t) * D + 4 * cg + e) : 0.f;
+    for (int e = 0; e < 4; ++e)
+      vr[t][e] = t < cnt ? ld_io<IO_BF16>(a.v, ((size_t)h * T + t) * D + 4 * cg + e) * inv : 0.f;
 
   char *Sh = (char *)a.state + (size_t)h * D * D * ES;
   for (int m0 = 0; m0 < RPL; m0 += U) {
     float s[U][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) ld_state4<ST_BF16>(Sh + (size_t)(rph + RP * (m0 + u)) * D * ES, cg, s[u]);
+    for (int u = 0; u < U; ++u) ld_state4<ST>(Sh + (size_t)(rph + RP * (m0 + u)) * D * ES, cg, s[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = rph + RP * (m0 + u);
@@ -227,12 +249,12 @@ __global__ __launch_bounds__(64 * kW) void commit_kernel(DecodeMultiArgs a) {
           for (int e = 0; e < 4; ++e) s[u][e] = fmaf(kv, vr[t][e], s[u][e]);
         }
       }
-      st_state4<ST_BF16>(Sh + (size_t)i * D * ES, cg, s[u]);
+      st_state4<ST>(Sh + (size_t)i * D * ES, cg, s[u]);
     }
   }
 }
 
-template <int D, bool IO, bool ST>
+template <int D, bool IO, int ST>
 hipError_t go(const DecodeMultiArgs &a, bool commit, hipStream_t stream) {
   if (commit) {
     const int64_t grid = (a.BH + kW - 1) / kW;
@@ -246,21 +268,27 @@ hipError_t go(const DecodeMultiArgs &a, bool commit, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t go_d(const DecodeMultiArgs &a, bool commit, bool io_bf16, bool st_bf16, hipStream_t stream) {
-  if (io_bf16) return st_bf16 ? go<D, true, true>(a, commit, stream) : go<D, true, false>(a, commit, stream);
-  return st_bf16 ? go<D, false, true>(a, commit, stream) : go<D, false, false>(a, commit, stream);
+template <int D, bool IO>
+hipError_t go_st(const DecodeMultiArgs &a, bool commit, int st, hipStream_t stream) {
+  switch (st) {
+    case kStF32: return go<D, IO, kStF32>(a, commit, stream);
+    case kStBF16: return go<D, IO, kStBF16>(a, commit, stream);
+    case kStE4M3: return go<D, IO, kStE4M3>(a, commit, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 int decode_multi_max_tokens() { return kTMax; }
 
-hipError_t decode_multi_launch(DecodeMultiArgs a, int d, bool commit, bool io_bf16, bool state_bf16,
+hipError_t decode_multi_launch(DecodeMultiArgs a, int d, bool commit, bool io_bf16, int state_fmt,
                                hipStream_t stream) {
   if (a.T < 1 || a.T > kTMax) return hipErrorInvalidValue;
-  if (d == 128) return go_d<128>(a, commit, io_bf16, state_bf16, stream);
-  if (d == 64) return go_d<64>(a, commit, io_bf16, state_bf16, stream);
+  if (d == 128)
+    return io_bf16 ? go_st<128, true>(a, commit, state_fmt, stream) : go_st<128, false>(a, commit, state_fmt, stream);
+  if (d == 64)
+    return io_bf16 ? go_st<64, true>(a, commit, state_fmt, stream) : go_st<64, false>(a, commit, state_fmt, stream);
   return hipErrorInvalidValue;
 }
 

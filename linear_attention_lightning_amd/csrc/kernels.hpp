@@ -89,9 +89,11 @@ struct DecodeMultiArgs {
   int64_t BH;
   int64_t H;
   int T;
+  const float *scale;     // [BH] per-sequence state scale (narrow formats; null = 1)
 };
 int decode_multi_max_tokens();
-hipError_t decode_multi_launch(DecodeMultiArgs a, int d, bool commit, bool io_bf16, bool state_bf16,
+// state_fmt: a StateFmt value
+hipError_t decode_multi_launch(DecodeMultiArgs a, int d, bool commit, bool io_bf16, int state_fmt,
                                hipStream_t stream);
 
 // State accumulation over a token segment: state += K^T V (no q, no outputs).

@@ -245,10 +245,11 @@ int lin_attn_prefill_recurrent(const void *q, const void *k, const void *v, void
 namespace {
 int decode_multi_impl(const void *q, const void *k, const void *v, void *o, void *state, const int32_t *accept,
                       bool commit, int64_t B, int64_t H, int64_t T, int64_t d, lin_attn_dtype_t io_dtype,
-                      lin_attn_dtype_t state_dtype, void *stream) {
+                      lin_attn_dtype_t state_dtype, void *stream, const float *scale = nullptr) {
   if (B < 0 || H < 0 || T < 0 || d < 0) return LIN_ATTN_EINVAL;
   if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
-  if (state_dtype != LIN_ATTN_F32 && state_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (state_dtype != LIN_ATTN_F32 && state_dtype != LIN_ATTN_BF16 && state_dtype != LIN_ATTN_FP8_E4M3)
+    return LIN_ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
   if (T > lal::decode_multi_max_tokens()) return LIN_ATTN_EUNSUPPORTED;
   int64_t BH, total;
@@ -257,12 +258,29 @@ int decode_multi_impl(const void *q, const void *k, const void *v, void *o, void
   if ((!commit && (!ok_ptr(q) || !ok_ptr(o))) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(state))
     return LIN_ATTN_EINVAL;
   if (accept != nullptr && ((uintptr_t)accept & 3u) != 0) return LIN_ATTN_EINVAL;
+  if (scale != nullptr && ((uintptr_t)scale & 3u) != 0) return LIN_ATTN_EINVAL;
   if ((BH + 1) / 2 > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
-  lal::DecodeMultiArgs a{q, k, v, o, state, accept, BH, H, (int)T};
-  return from_hip(lal::decode_multi_launch(a, (int)d, commit, io_dtype == LIN_ATTN_BF16,
-                                           state_dtype == LIN_ATTN_BF16, (hipStream_t)stream));
+  lal::DecodeMultiArgs a{q, k, v, o, state, accept, BH, H, (int)T, scale};
+  return from_hip(lal::decode_multi_launch(a, (int)d, commit, io_dtype == LIN_ATTN_BF16, state_fmt_of(state_dtype),
+                                           (hipStream_t)stream));
 }
 }  // namespace
+
+int lin_attn_decode_verify_scaled(const void *q, const void *k, const void *v, void *o, const void *state,
+                                  const float *state_scale, int64_t B, int64_t H, int64_t T, int64_t d,
+                                  lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream) {
+  if (state_dtype == LIN_ATTN_F32) return LIN_ATTN_EUNSUPPORTED;
+  return decode_multi_impl(q, k, v, o, const_cast<void *>(state), nullptr, false, B, H, T, d, io_dtype,
+                           state_dtype, stream, state_scale);
+}
+
+int lin_attn_decode_commit_scaled(const void *k, const void *v, void *state, const float *state_scale,
+                                  const int32_t *accept, int64_t B, int64_t H, int64_t T, int64_t d,
+                                  lin_attn_dtype_t io_dtype, lin_attn_dtype_t state_dtype, void *stream) {
+  if (state_dtype == LIN_ATTN_F32) return LIN_ATTN_EUNSUPPORTED;
+  return decode_multi_impl(nullptr, k, v, nullptr, state, accept, true, B, H, T, d, io_dtype, state_dtype,
+                           stream, state_scale);
+}
 
 int lin_attn_decode_verify(const void *q, const void *k, const void *v, void *o, const void *state, int64_t B,
                            int64_t H, int64_t T, int64_t d, lin_attn_dtype_t io_dtype,

@@ -159,6 +159,30 @@ def test_scaled_state_validation_codes():
             assert pre(q=None, st=st, rc=rc, sc=None) == la.EINVAL  # passes every size check
 
 
+def test_scaled_verify_commit_validation_codes():
+    lib = la.library()
+
+    def ver(q=FAKE, s=FAKE, sc=None, B=1, H=1, T=4, d=128, io=la.BF16, st=la.FP8_E4M3):
+        return lib.lin_attn_decode_verify_scaled(q, FAKE, FAKE, FAKE, s, sc, B, H, T, d, io, st, None)
+
+    def com(s=FAKE, sc=None, acc=None, B=1, H=1, T=4, d=128, io=la.BF16, st=la.FP8_E4M3):
+        return lib.lin_attn_decode_commit_scaled(FAKE, FAKE, s, sc, acc, B, H, T, d, io, st, None)
+
+    for f in (ver, com):
+        assert f(st=la.F32) == la.EUNSUPPORTED
+        assert f(st=7) == la.EUNSUPPORTED
+        assert f(T=17) == la.EUNSUPPORTED
+        assert f(B=-1) == la.EINVAL
+        assert f(s=None) == la.EINVAL
+        assert f(sc=FAKE + 2) == la.EINVAL
+        assert f(T=0, s=None) == la.OK
+    assert ver(q=None) == la.EINVAL
+    assert com(acc=FAKE + 1) == la.EINVAL
+    # the unscaled calls accept an FP8 state (unit scales)
+    assert lib.lin_attn_decode_verify(None, FAKE, FAKE, FAKE, FAKE, 1, 1, 4, 128, la.BF16, la.FP8_E4M3, None) == la.EINVAL
+    assert lib.lin_attn_decode_commit(FAKE, FAKE, FAKE, None, 1, 1, 4, 96, la.BF16, la.FP8_E4M3, None) == la.EUNSUPPORTED
+
+
 def test_backward_validation_codes():
     lib = la.library()
 

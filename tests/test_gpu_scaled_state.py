@@ -299,3 +299,97 @@ def test_prefill_scaled_carry_rounding(fmt, d, N, block, H):
     np.testing.assert_array_equal(codes_full, codes)
     np.testing.assert_array_equal(o_full, np.concatenate(outs, axis=2))
     print(f"  blocks: {len(outs)}, midpoint flips: {flips}")
+
+
+# ------------------------------------------------ verify / commit drafts ----
+
+@pytest.mark.parametrize("fmt", ["e4m3", "bf16"])
+@pytest.mark.parametrize("d,T,io", [(128, 4, "bf16"), (128, 16, "fp32"), (64, 7, "bf16"), (64, 1, "fp32")])
+def test_verify_scaled(fmt, d, T, io):
+    """Draft outputs from a narrow stored state with per-sequence scales
+    equal the oracle run from the widened state; the state is untouched."""
+    announce("verify scaled", fmt, d, T, io)
+    B, H = 2, 3
+    scale = scales_for((B, H), "pow2")
+    codes = decode_case(20 + T, B, H, d, io, fmt, scale)
+    q, k, v = synth.prefill_inputs(80 + T, B, H, T, d, io)
+    o_ref, _ = oracle.recurrence(q, k, v, oracle.stored_to_f64(codes, FMTS[fmt], scale))
+    Sd = to_device_codes(codes, fmt)
+    od = torch.empty((B, H, T, d), dtype=dev(q, io).dtype, device="cuda")
+    la.decode_verify(dev(q, io), dev(k, io), dev(v, io), od, Sd, state_scale=torch.from_numpy(scale).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host_codes(Sd, fmt), codes)
+    e = rel_err(host(od), o_ref)
+    print(f"  rel err o={e:.3e}")
+    assert e <= TOL_IO[io]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "bf16"])
+@pytest.mark.parametrize("d,T", [(128, 4), (64, 16)])
+def test_commit_scaled(fmt, d, T):
+    """Commit of per-sequence accepted counts (0 .. T, clamped): the stored
+    state is the oracle's single rounding of the widened state plus the
+    accepted drafts, up to fp32 midpoint ties; accepting 0 leaves it
+    bit-identical."""
+    announce("commit scaled", fmt, d, T)
+    B, H = 4, 2
+    scale = scales_for((B, H), "pow2")
+    codes = decode_case(30 + T, B, H, d, "bf16", fmt, scale)
+    _, k, v = synth.prefill_inputs(90 + T, B, H, T, d, "bf16")
+    v = v * 4.0  # updates comparable to a stored-code step
+    accept = np.array([0, 1, T, T + 5], np.int32)
+    Sd = to_device_codes(codes, fmt)
+    la.decode_commit(dev(k, "bf16"), dev(v, "bf16"), Sd, torch.from_numpy(accept).cuda(),
+                     state_scale=torch.from_numpy(scale).cuda())
+    torch.cuda.synchronize()
+    got = to_host_codes(Sd, fmt)
+    S_in = oracle.stored_to_f64(codes, FMTS[fmt], scale)
+    for b in range(B):
+        a_b = int(min(max(accept[b], 0), T))
+        if a_b == 0:
+            np.testing.assert_array_equal(got[b], codes[b])
+            continue
+        S_exact = oracle.state_after(k[b, :, :a_b], v[b, :, :a_b], S_in[b])
+        # fp32 sums of up to 16 terms: a few fp32 ulps from the exact value
+        n = check_codes(got[b], S_exact, fmt, scale[b], rel_tol=2.0 ** -19,
+                        abs_tol=1e-6 * float(np.max(np.abs(S_exact / scale[b][:, None, None]))))
+        print(f"  batch {b}: accepted {a_b}, midpoint flips {n}")
+
+
+def test_verify_commit_fp8_unit_scale_is_plain_entry():
+    """The unscaled verify and commit with an FP8 state are the scaled ones
+    with unit scales, bit for bit."""
+    announce("verify/commit fp8 plain entry vs unit scales")
+    B, H, T, d = 2, 3, 5, 128
+    codes = decode_case(40, B, H, d, "bf16", "e4m3", None)
+    q, k, v = synth.prefill_inputs(95, B, H, T, d, "bf16")
+    ones = torch.ones((B, H), device="cuda")
+    outs, states = [], []
+    for sc in (None, ones):
+        Sd = to_device_codes(codes, "e4m3")
+        od = torch.empty((B, H, T, d), dtype=torch.bfloat16, device="cuda")
+        la.decode_verify(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), od, Sd, state_scale=sc)
+        la.decode_commit(dev(k, "bf16"), dev(v, "bf16"), Sd, state_scale=sc)
+        torch.cuda.synchronize()
+        outs.append(od.view(torch.int16).cpu())
+        states.append(to_host_codes(Sd, "e4m3"))
+    assert torch.equal(outs[0], outs[1])
+    np.testing.assert_array_equal(states[0], states[1])
+
+
+def test_commit_fp8_exact_integers():
+    """Integer states and drafts within E4M3's exact range: the committed
+    state equals the oracle's bitwise, for every accepted count."""
+    announce("commit fp8 exact integers")
+    B, H, T, d = 3, 2, 6, 128
+    rng = np.random.default_rng(77)
+    S = rng.integers(-3, 4, (B, H, d, d)).astype(np.float64)
+    _, k, v = synth.integer_inputs(777, B, H, T, d)
+    assert (np.abs(S) + np.einsum("bhti,bhtj->bhij", np.abs(k), np.abs(v))).max() <= 16
+    accept = np.array([2, 0, 6], np.int32)
+    Sd = to_device_codes(oracle.round_to_stored(S, oracle.FMT_E4M3), "e4m3")
+    la.decode_commit(dev(k, "bf16"), dev(v, "bf16"), Sd, torch.from_numpy(accept).cuda())
+    torch.cuda.synchronize()
+    got = oracle.stored_to_f64(to_host_codes(Sd, "e4m3"), oracle.FMT_E4M3)
+    for b in range(B):
+        np.testing.assert_array_equal(got[b], oracle.state_after(k[b, :, :accept[b]], v[b, :, :accept[b]], S[b]))
