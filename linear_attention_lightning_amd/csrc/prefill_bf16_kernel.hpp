@@ -25,8 +25,7 @@
 //    buffer descriptor covers exactly the valid rows, so rows past the end of
 //    the sequence arrive as zeros -- ragged tails need no other masking.
 //  * Q rows are loaded by each wave straight into the registers that feed the
-//    matrix cores, one block ahead (issued after the output phase, so that
-//    they occupy registers only during the state update).
+//    matrix cores, one block ahead.
 //  * LDS tiles are unpadded with an XOR swizzle of their 16-byte chunks,
 //    chosen so that 16-byte fragment reads (one row per lane) and the
 //    transposing 8-byte reads both run without bank conflicts.
@@ -625,13 +624,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
   };
 
-  // ---- one block.  On entry the direct loads of block jblk (into Kc, Vc)
-  // and its Q rows (issued interleaved), then the output stores of block
-  // jblk-1, may be in flight; the other stage (Kn, Vn) is free (its block's
-  // reads ended at the previous block's second barrier).  During the block
-  // the wave issues, spread over its matrix work so that no burst stalls it
-  // on a full memory queue: the Q rows and K/V tiles of block jblk+1 (in
-  // phase A) and this block's output stores (in phase B). ----
+  // ---- one block.  On entry the Q rows and direct loads of block jblk
+  // (into Kc, Vc), then the output stores of block jblk-1, may be in flight;
+  // the other stage (Kn, Vn) is free (its block's reads ended at the previous
+  // block's second barrier).  During the block the wave issues the Q rows of
+  // block jblk+1 (at the start), its K/V tiles (spread over the matrix work
+  // of phase A, so that no burst stalls the wave on a full memory queue) and
+  // this block's output stores (spread over phase B). ----
   auto body = [&](int jblk, const u16 *Kc, const u16 *Vc, u16 *Kn, u16 *Vn) __attribute__((always_inline)) {
     // (in forward order the reversed arms fold away at compile time, leaving
     // exactly the forward kernel's code)
@@ -649,11 +648,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
     // the next block's loads, one share per issue slot
     const KvDma dma = kv_prepare(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, Kn, Vn);
+    // The next block's Q rows, issued here in code that every wave runs: issued
+    // inside the per-row-tile branches of phase A, their destination registers
+    // differ between branches, and the compiler's wait analysis, which merges
+    // the branches, then drains all loads in flight at the start of phase A.
+#pragma unroll
+    for (int kc = 0; kc < P::NKC; ++kc) {
+      load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 0, kc);
+      load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 1, kc);
+    }
     auto vm_slot = [&](int slot) __attribute__((always_inline)) {
-      if (slot < P::NKC) {
-        load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 0, slot);
-        load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 1, slot);
-      }
       if (nlen > 0) {
 #pragma unroll
         for (int m = slot * P::N_DMA / P::NSLOT; m < (slot + 1) * P::N_DMA / P::NSLOT; ++m) kv_issue(dma, m);
