@@ -228,6 +228,11 @@ struct Plan {
   static constexpr int CG0 = kWaves / RG;
   static constexpr int CG = CG0 < NJ ? CG0 : NJ;
   static constexpr int NJC = NJ / CG;
+  // output stores per block and wave: pairs of value tiles are written
+  // together, 16 bytes per lane (see store_o_pair), when a wave has an even
+  // number of them
+  static constexpr bool PAIR = NJC % 2 == 0;
+  static constexpr int NST = PAIR ? NJC : 2 * NJC;
   static constexpr int AWAVES = RG * CG;
   // phase B: PBR x PBC grid of waves over the state tiles
   static constexpr int PBR = kWaves < 4 ? kWaves : 4;
@@ -624,6 +629,36 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
   };
 
+  // Value tiles 2 jp and 2 jp + 1 of row tile u in one store.  In the
+  // matrix-core output layout lane (lr, g) holds 4 consecutive values (8
+  // bytes) of token 16 T_u + lr in each tile, so an output row would be
+  // written in 32-byte pieces.  Two lane swaps across the four 16-lane rows
+  // (the upper 32 lanes of one tile with the lower 32 of the other, then the
+  // odd rows of one with the even rows of the other) leave lane (lr, g) with
+  // values 8 g .. 8 g + 7 of the pair (16 bytes), so each row of the pair is
+  // written as 64 contiguous bytes: half the store instructions, and half
+  // the write requests, each holding an L1 slot.
+  auto store_o_pair = [&](int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jp)
+                          __attribute__((always_inline)) {
+    const u32x4 dod = raw_desc(oh + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
+    __amdgpu_buffer_rsrc_t ro;
+    __builtin_memcpy(&ro, &dod, sizeof(ro));
+    const uint2 ta = packed[u][2 * jp], tb = packed[u][2 * jp + 1];
+    const auto x1 = __builtin_amdgcn_permlane32_swap(ta.x, tb.x, false, false);
+    const auto y1 = __builtin_amdgcn_permlane32_swap(ta.y, tb.y, false, false);
+    const auto x2 = __builtin_amdgcn_permlane16_swap(x1[0], x1[1], false, false);
+    const auto y2 = __builtin_amdgcn_permlane16_swap(y1[0], y1[1], false, false);
+    const u32x4 data = {x2[0], y2[0], x2[1], y2[1]};
+    const LaneOff lo_st = lane_off();
+    if constexpr (REV) {
+      const int orow = len - 1 - 16 * (u ? T1 : T0) - lo_st.lr;
+      __builtin_amdgcn_raw_buffer_store_b128(data, ro, (orow * D + jc0 * 16) * 2 + 16 * lo_st.g + jp * 64, 0, 0);
+    } else {
+      const int olane = (lo_st.lr * D + jc0 * 16) * 2 + 16 * lo_st.g;
+      __builtin_amdgcn_raw_buffer_store_b128(data, ro, olane + jp * 64, 16 * (u ? T1 : T0) * D * 2, 0);
+    }
+  };
+
   // ---- one block.  On entry the Q rows and direct loads of block jblk
   // (into Kc, Vc), then the output stores of block jblk-1, may be in flight;
   // the other stage (Kn, Vn) is free (its block's reads ended at the previous
@@ -639,7 +674,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const int nlen = jblk + 1 < nblk ? block_len(jblk + 1) : 0;
     // Wait for this block's tiles and Q rows; the previous block's 2 NJC
     // output stores, issued after them, may stay in flight.
-    wait_vmcnt(jblk == 0 ? 0 : 2 * P::NJC);
+    wait_vmcnt(jblk == 0 ? 0 : P::NST);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -695,8 +730,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int c0 = 32 * cc;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = cc * 2 * P::NJC / P::NCC; i < (cc + 1) * 2 * P::NJC / P::NCC; ++i)
-        store_o_part(tok0, len, packed, i / P::NJC, i % P::NJC);
+      for (int i = cc * P::NST / P::NCC; i < (cc + 1) * P::NST / P::NCC; ++i) {
+        if constexpr (P::PAIR)
+          store_o_pair(tok0, len, packed, i / (P::NJC / 2), i % (P::NJC / 2));
+        else
+          store_o_part(tok0, len, packed, i / P::NJC, i % P::NJC);
+      }
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 ka[P::BIT], vb[P::BJT];
 #pragma unroll
