@@ -232,7 +232,9 @@ struct Plan {
   // together, 16 bytes per lane (see store_o_pair), when a wave has an even
   // number of them
   static constexpr bool PAIR = NJC % 2 == 0;
-  static constexpr int NST = PAIR ? NJC : 2 * NJC;
+  static constexpr bool QUAD = NJC % 4 == 0;  // whole 128-byte lines (store_o_quad)
+  static constexpr int NST = PAIR ? NJC : 2 * NJC;            // store instructions
+  static constexpr int NSTI = QUAD ? NJC / 2 : NST;            // store calls (a quad call issues 2)
   static constexpr int AWAVES = RG * CG;
   // phase B: PBR x PBC grid of waves over the state tiles
   static constexpr int PBR = kWaves < 4 ? kWaves : 4;
@@ -659,6 +661,52 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
   };
 
+  // Value tiles 4 jq .. 4 jq + 3 of row tile u in two stores that each write
+  // 128 contiguous bytes -- one whole line -- for 8 of the 16 tokens.  After
+  // the pair rearrangement of store_o_pair, lane (lr, g) holds 16 bytes of
+  // pair A (tiles 4 jq, 4 jq + 1; bytes 0..63 of its token's span) and of pair
+  // B (bytes 64..127).  Lanes lr and lr ^ 8 of a 16-lane row then trade one of
+  // them (a rotation by 8 within the row): store h writes tokens 8 h .. 8 h + 7,
+  // the lanes lr < 8 holding bytes 0..63 and the lanes lr >= 8 bytes 64..127.
+  auto store_o_quad = [&](int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jq)
+                          __attribute__((always_inline)) {
+    const u32x4 dod = raw_desc(oh + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
+    __amdgpu_buffer_rsrc_t ro;
+    __builtin_memcpy(&ro, &dod, sizeof(ro));
+    u32x4 pr[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint2 ta = packed[u][4 * jq + 2 * h], tb = packed[u][4 * jq + 2 * h + 1];
+      const auto x1 = __builtin_amdgcn_permlane32_swap(ta.x, tb.x, false, false);
+      const auto y1 = __builtin_amdgcn_permlane32_swap(ta.y, tb.y, false, false);
+      const auto x2 = __builtin_amdgcn_permlane16_swap(x1[0], x1[1], false, false);
+      const auto y2 = __builtin_amdgcn_permlane16_swap(y1[0], y1[1], false, false);
+      pr[h] = u32x4{x2[0], y2[0], x2[1], y2[1]};
+    }
+    const LaneOff lo_st = lane_off();
+    const bool upper = lo_st.lr >= 8;
+    const int col = (jc0 * 16) * 2 + jq * 128 + (lo_st.lr >> 3) * 64 + 16 * lo_st.g;  // byte in the slice row
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // store h: the lower lanes keep pair A (h = 0) or take the partner's
+      // pair A (h = 1); the upper lanes take the partner's pair B (h = 0) or
+      // keep their own (h = 1)
+      u32x4 data;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int moved = __builtin_amdgcn_update_dpp(0, (int)pr[1 - h][w], 0x128 /* row_ror:8 */, 0xf, 0xf, false);
+        data[w] = (upper == (h == 0)) ? (uint32_t)moved : pr[h][w];
+      }
+      const int tok = 8 * h + (lo_st.lr & 7);  // token within the row tile
+      if constexpr (REV) {
+        const int orow = len - 1 - 16 * (u ? T1 : T0) - tok;
+        __builtin_amdgcn_raw_buffer_store_b128(data, ro, orow * D * 2 + col, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(data, ro, tok * D * 2 + col, 16 * (u ? T1 : T0) * D * 2, 0);
+      }
+    }
+  };
+
   // ---- one block.  On entry the Q rows and direct loads of block jblk
   // (into Kc, Vc), then the output stores of block jblk-1, may be in flight;
   // the other stage (Kn, Vn) is free (its block's reads ended at the previous
@@ -730,8 +778,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int c0 = 32 * cc;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = cc * P::NST / P::NCC; i < (cc + 1) * P::NST / P::NCC; ++i) {
-        if constexpr (P::PAIR)
+      for (int i = cc * P::NSTI / P::NCC; i < (cc + 1) * P::NSTI / P::NCC; ++i) {
+        if constexpr (P::QUAD)
+          store_o_quad(tok0, len, packed, i / (P::NJC / 4), i % (P::NJC / 4));
+        else if constexpr (P::PAIR)
           store_o_pair(tok0, len, packed, i / (P::NJC / 2), i % (P::NJC / 2));
         else
           store_o_part(tok0, len, packed, i / P::NJC, i % P::NJC);
