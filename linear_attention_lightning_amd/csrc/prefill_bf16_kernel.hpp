@@ -222,7 +222,7 @@ struct Plan {
   static constexpr int CPRV = DV / 8;  // per V-slice row
   static constexpr int NJ = DV / 16;
   static constexpr int NI = D / 16;
-  static constexpr int NKC = D / 32;
+  static constexpr int NKC = D / 32;  // even: the Q rows load in pairs of steps
   static constexpr int BLKP = NT * 16;  // staged rows per block, a multiple of 32
   static constexpr int NCC = BLKP / 32;
   // phase A: RG row-tile pairs x CG column groups
@@ -261,6 +261,7 @@ struct Plan {
   static constexpr int NCH_MIN = (NT / 2) / 2 + 1;
   static constexpr int NSLOT = NKC + NCH_MIN;
   static_assert(NT % 2 == 0 && NT >= 2 && NT <= 8, "2..8 row tiles per block");
+  static_assert(NKC % 2 == 0, "whole-line Q loads");
   static_assert(NJ % CG == 0 && AWAVES <= kWaves, "phase A grid");
   static_assert(BIT >= 1 && BJT >= 1, "phase B grid");
   static_assert(BLKP % KRPI == 0 && BLKP % VRPI == 0, "direct-load rows");
@@ -387,8 +388,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     o.rr = 4 * o.g + (o.lr >> 2);  // row of a transposing read within 16
     return o;
   };
-  // 16-byte fragment of row lr, chunk 4kc+g (K rows and the state copy)
-  auto kfrag = [&](const LaneOff &o, int kc) { return o.lr * RB + (swz<P::CPRK>(o.lr, 4 * kc + o.g) << 4); };
+  // 16-byte fragment of row lr for contraction step kc (K rows and the state
+  // copy).  Step kc takes from 128-byte line kc/2 of the row the chunks of
+  // parity kc%2, chunk 2g + kc%2 for lane group g, rather than four adjacent
+  // chunks: the contraction over the head dimension may run in any order
+  // that all its operands share, and in this one the Q rows load as whole
+  // lines (see load_q_part).
+  auto kfrag = [&](const LaneOff &o, int kc) {
+    return o.lr * RB + (swz<P::CPRK>(o.lr, 8 * (kc >> 1) + 2 * o.g + (kc & 1)) << 4);
+  };
   // transposing-read operand of value tile jt (V) and key tile it (K^T)
   auto vtr = [&](const LaneOff &o, int jt) { return o.rr * VRB + (swz<P::CPRV>(o.rr, 2 * jt + o.h) << 4) + o.lo8; };
   auto ktr = [&](const LaneOff &o, int it) { return o.rr * RB + (swz<P::CPRK>(o.rr, 2 * it + o.h) << 4) + o.lo8; };
@@ -419,23 +427,53 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // that every wave issues the same vector-memory operations.
   const int T0 = rg, T1 = NT - 1 - rg;
   // (cache policy 2: non-temporal, as the K/V tiles -- Q rows are read once)
-  auto load_q_part = [&](int64_t tok0, int len, int u, int kc) __attribute__((always_inline)) {
+  // Load m = 2l + h of row tile u reads rows 8h..8h+7 of the tile, 128-byte
+  // line l of each: lane (lr, g) takes row 8h + (lr & 7), chunk 2g + (lr >> 3)
+  // of the line.  Each row's line is read by one instruction, so the L1 sends
+  // it to L2 as one 128-byte request; the operand fragments are rearranged
+  // from these registers at the start of the block that uses them (take_q).
+  auto load_q_part = [&](int64_t tok0, int len, int u, int m) __attribute__((always_inline)) {
     // descriptor built from scalar-forced words: with the generic builder the
     // compiler could not prove it uniform and looped over lanes per load
     const u32x4 dq = raw_desc(qh + (size_t)tok0 * D, act ? (uint32_t)len * D * 2 : 0u);
     __amdgpu_buffer_rsrc_t rq;
     __builtin_memcpy(&rq, &dq, sizeof(rq));
     const LaneOff lo = lane_off();
+    const int l = m >> 1, h = m & 1;
+    const int col = 16 * lo.g + 8 * (lo.lr >> 3);  // element within the line
     if constexpr (REV) {
-      // row 16 T + lr is token len-1-16T-lr of the span (negative: padding)
-      const int qrow = len - 1 - 16 * (u ? T1 : T0) - lo.lr;
-      qn[u][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rq, (qrow * D + 8 * lo.g) * 2, kc * 64, 2));
+      // row 16 T + r is token len-1-16T-r of the span (negative: padding)
+      const int qrow = len - 1 - 16 * (u ? T1 : T0) - 8 * h - (lo.lr & 7);
+      qn[u][m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rq, (qrow * D + col) * 2, l * 128, 2));
     } else {
-      const int qlane = (lo.lr * D + 8 * lo.g) * 2;  // Q fragment of row lr
-      qn[u][kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rq, qlane, (16 * (u ? T1 : T0) * D + kc * 32) * 2, 2));
+      const int qlane = ((lo.lr & 7) * D + col) * 2;
+      qn[u][m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rq, qlane, ((16 * (u ? T1 : T0) + 8 * h) * D + 64 * l) * 2, 2));
     }
+  };
+  // Operand fragments from the loaded lines.  Step 2l (chunk 2g of line l for
+  // lane group g) is, for rows lr < 8, what load 2l holds in the same lane
+  // and, for rows 8..15, what load 2l+1 holds in lane lr ^ 8; step 2l+1 the
+  // other way round.  A row rotation by 8 (DPP row_ror:8) written only to the
+  // lanes of the upper (bank mask 0xc) or the lower (0x3) half of each row
+  // does each in one move per dword.
+  auto take_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int l = 0; l < P::NKC / 2; ++l) {
+        const u32x4 a = __builtin_bit_cast(u32x4, qn[u][2 * l]);
+        const u32x4 b = __builtin_bit_cast(u32x4, qn[u][2 * l + 1]);
+        u32x4 e, o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          e[w] = (uint32_t)__builtin_amdgcn_update_dpp((int)a[w], (int)b[w], 0x128 /* row_ror:8 */, 0xf, 0xc, false);
+          o[w] = (uint32_t)__builtin_amdgcn_update_dpp((int)b[w], (int)a[w], 0x128 /* row_ror:8 */, 0xf, 0x3, false);
+        }
+        bq[u][2 * l] = __builtin_bit_cast(bf16x8, e);
+        bq[u][2 * l + 1] = __builtin_bit_cast(bf16x8, o);
+      }
   };
   auto load_q = [&](int64_t tok0, int len) __attribute__((always_inline)) {
 #pragma unroll
@@ -726,10 +764,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // Wait for this block's tiles and Q rows; the previous block's 2 NJC
     // output stores, issued after them, may stay in flight.
     wait_vmcnt(jblk == 0 ? 0 : P::NST);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int kc = 0; kc < P::NKC; ++kc) bq[u][kc] = qn[u][kc];
+    take_q();
     lds_barrier();  // every wave's tiles of block jblk and the state copy are in LDS
 
     // the next block's loads, one share per issue slot
