@@ -21,6 +21,9 @@ heads) over the timed steps.  Prints ONE JSON line.
 
 ``--only crossover`` sweeps the chunked and the token-by-token prefill over
 N = 256 ... 32768 at the crossover shape (see crossover_sweep).
+``--only ceiling`` measures the HBM bandwidth a plain streaming kernel
+reaches for the path's read:write byte mixes (see hbm_ceiling); the default
+run includes it.
 ``--only drift`` instead measures the rounding drift of stored states against
 the fp64 oracle along one 1M-token sequence (not part of a step; see
 drift_report).
@@ -55,6 +58,7 @@ DRAFTS = 4      # draft tokens verified per sequence in the speculative step
 PREFILL_KERNEL_SOURCES = ["linear_attention_lightning_amd/csrc/prefill_bf16_kernel.hpp",
                           "linear_attention_lightning_amd/csrc/prefill_bf16.hip",
                           "linear_attention_lightning_amd/csrc/common.hpp"]
+PROBE_LIB = os.path.join(ROOT, "linear_attention_lightning_amd", "_lib", "libhbm_stream.so")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_B4_H64_N32768_d128_blk128_hbm_traffic.md")
 
 
@@ -154,13 +158,61 @@ def cpu_baseline(heads: int = 64, min_seconds: float = 10.0, max_passes: int = 6
     }
 
 
+def hbm_ceiling(torch, reps: int = 5):
+    """Practical HBM ceiling of each traffic mix of the path, from a plain
+    streaming kernel (csrc/hbm_stream.hip, its own library): 16-byte
+    non-temporal loads, consecutive lanes at consecutive addresses, one
+    contiguous run of 4 KiB units per workgroup.  Measured for reads only,
+    for 3 bytes read per byte written (the prefill's mix: q, k, v in, o out)
+    and for 1:1 (the decode step's state read and write), each the best
+    average over grid sizes and store policies.  HIP events on the launch
+    stream, `reps` timed launches after 2 untimed ones."""
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.hbm_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    read_bytes = 6 << 30
+    src = torch.ones(read_bytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.zeros(3 << 28, dtype=torch.int32, device=dev)  # 3 GiB
+    unit = 4096
+    mixes = {"read_only": (1, 0, read_bytes // unit), "r3w1": (3, 1, read_bytes // (3 * unit)),
+             "r1w1": (1, 1, (3 << 30) // unit)}
+    out = {}
+    for name, (rd, wr, units) in mixes.items():
+        moved = units * unit * (rd + wr)
+        best = None
+        for nt in ((0, 1) if wr else (0,)):
+            for wgs in (2048, 8192, 16384):
+                ms = []
+                for i in range(reps + 2):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    rc = lib.hbm_stream(src.data_ptr(), dst.data_ptr(), units, rd, wr, nt, wgs, stream.cuda_stream)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    if rc != 0:
+                        raise RuntimeError(f"hbm_stream returned {rc}")
+                    if i >= 2:
+                        ms.append(e0.elapsed_time(e1))
+                gbs = moved / (sum(ms) / len(ms) / 1e3) / 1e9
+                if best is None or gbs > best[0]:
+                    best = (gbs, nt, wgs)
+        out[name + "_GBps"] = best[0]
+        out[name + "_config"] = f"nt_store={best[1]} workgroups={best[2]}"
+    del src, dst
+    out["kernel"] = "plain streaming kernel, 16-byte non-temporal loads, 256-lane workgroups (csrc/hbm_stream.hip)"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy", "drift", "crossover"],
+    ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy", "drift", "crossover",
+                                       "ceiling"],
                     help="run one kernel only (for counter collection); prints timings, no JSON")
     args = ap.parse_args()
 
@@ -188,6 +240,9 @@ def main():
         print(json.dumps(crossover_sweep(la, synth, torch, steps=args.steps)))
         return
 
+    if args.only == "ceiling":
+        print(json.dumps(hbm_ceiling(torch)))
+        return
     if args.only == "copy":
         # plain copy of a known size, used to calibrate the HBM byte counters
         n = 1 << 30
@@ -315,6 +370,7 @@ def main():
             print(f"{n}: avg {avg[n]:.4f} ms, min {best[n]:.4f} ms over {args.steps} launches")
         return
 
+    ceiling = hbm_ceiling(torch)
     p_bytes = prefill_bytes(**P)
     p_flops = prefill_flops(**P)
     p_dense = prefill_dense_flops(**P)
@@ -380,6 +436,8 @@ def main():
             "e4m3_state_ms": avg["decode_e4m3"], "e4m3_state_GBps": d8_bytes / (avg["decode_e4m3"] / 1e3) / 1e9,
             "e4m3_state_pct_hbm_peak": 100 * d8_bytes / (avg["decode_e4m3"] / 1e3) / 1e9 / PEAK_HBM_GBS,
             "tokens_per_s_fp32_state": D["B"] / (avg["decode_fp32"] / 1e3),
+            "fp32_state_pct_of_1to1_stream_ceiling": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9
+            / ceiling["r1w1_GBps"],
             "speculative": {
                 "drafts": DRAFTS, "accepted": DRAFTS - 1,
                 "verify_ms": avg["verify"], "commit_ms": avg["commit"],
@@ -410,7 +468,12 @@ def main():
             "frac": gbs / PEAK_HBM_GBS,
             "traffic": traffic,
             "algorithmic_bytes": p_bytes,
+            # the best rate a plain streaming kernel reaches for the same 3:1
+            # read:write mix on this GPU (hbm_ceiling), and the share of it
+            "practical_peak_same_mix": ceiling["r3w1_GBps"],
+            "frac_of_practical_peak": gbs / ceiling["r3w1_GBps"],
         },
+        "hbm_ceiling": ceiling,
         "timing": {"wall_ms_timed_region": wall_ms, "setup_s": setup_s,
                    "method": "HIP events on the launch stream around each kernel"},
     }

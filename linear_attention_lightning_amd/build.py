@@ -2,7 +2,10 @@
 
 Usage: ``python -m linear_attention_lightning_amd.build`` (or ``build()``).
 Every HIP source is compiled by hipcc for gfx950 only; the objects are linked
-into one shared library that exports the C ABI of include/lin_attn.h.
+into one shared library that exports the C ABI of include/lin_attn.h.  A
+second, separate library ``_lib/libhbm_stream.so`` holds the streaming
+bandwidth probe that bench.py measures the HBM ceiling of a traffic mix with
+(csrc/hbm_stream.h); the attention library does not contain it.
 """
 from __future__ import annotations
 
@@ -18,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "liblin_attn.so")
+PROBE_LIB = os.path.join(OUT_DIR, "libhbm_stream.so")
+PROBE_SOURCES = ["hbm_stream.hip"]
 SOURCES = ["lin_attn_api.hip", "prefill_bf16.hip", "prefill_bf16_scaled.hip", "prefill_bf16_grad.hip", "prefill_f32.hip", "decode.hip", "recurrent.hip",
            "state_delta.hip", "decode_multi.hip"]
 
@@ -51,21 +56,27 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    obj_dir = os.path.join(ROOT, "_build")
-    os.makedirs(obj_dir, exist_ok=True)
-    os.makedirs(OUT_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(os.cpu_count() or 1, 8)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    obj_dir = os.path.join(ROOT, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, min(os.cpu_count() or 1, 8)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, obj_dir), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -1,0 +1,34 @@
+/* Streaming bandwidth probe (measurement only; not part of the attention
+ * library, built separately as libhbm_stream.so).
+ *
+ * hbm_stream: one launch of a plain streaming kernel on `stream`.
+ *   src, dst      device pointers, 16-byte aligned, owned by the caller.
+ *   units         work units of 4096 bytes per read slice: the kernel reads
+ *                 units * reads_per_write * 4096 bytes of src and, when
+ *                 `write` is non-zero, writes units * 4096 bytes of dst
+ *                 (src must hold the former, dst the latter; a read-only run
+ *                 may store 4096 bytes to dst).
+ *   reads_per_write  1 or 3 with writes, 1 without.
+ *   nt_store      non-zero: non-temporal stores.
+ *   workgroups    workgroups of 256 lanes, each taking a contiguous run of units.
+ * Returns 0, -1 for a null pointer or a bad size, -2 for an unsupported
+ * combination, -3 for a launch error.
+ */
+#ifndef HBM_STREAM_H
+#define HBM_STREAM_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int hbm_stream(const void *src, void *dst, int64_t units, int reads_per_write, int write, int nt_store,
+               int workgroups, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -279,3 +279,18 @@ def test_decode_multi_validation_codes():
     assert ver(o=MISALIGNED) == la.EINVAL
     assert com(k=None) == la.EINVAL
     assert com(acc=FAKE + 2) == la.EINVAL   # accept must be 4-byte aligned
+
+
+def test_stream_probe_is_a_separate_library():
+    """The bandwidth probe that bench.py uses lives in its own library: it
+    exports hbm_stream, rejects bad arguments on the host, and the attention
+    library does not contain it."""
+    probe = os.path.join(os.path.dirname(la.LIB_PATH), "libhbm_stream.so")
+    lib = ctypes.CDLL(probe)
+    lib.hbm_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.hbm_stream(None, FAKE, 1, 1, 1, 0, 1, None) == -1
+    assert lib.hbm_stream(FAKE, FAKE, -1, 1, 1, 0, 1, None) == -1
+    assert lib.hbm_stream(FAKE, FAKE, 0, 3, 1, 0, 1, None) == 0  # nothing to do: no launch
+    nm = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True, check=True)
+    assert "hbm_stream" not in nm.stdout
