@@ -306,6 +306,10 @@ def main():
         hS0 = torch.zeros((SH["B"], SH["H"], SH["d"], SH["d"]), dtype=torch.float32, device=dev)
         la.state_accumulate(hk, hv, hS0)
         hdS = torch.zeros_like(hS0)
+        hdS2 = torch.zeros_like(hS0)
+        hws = torch.empty(max(16, la.state_accumulate_split_workspace(SH["B"], SH["H"], SH["N"], SH["d"],
+                                                                      torch.bfloat16)),
+                          dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
 
@@ -316,6 +320,7 @@ def main():
                              ("verify", need["decode"]),
                              ("commit", need["decode"]), ("small_chunked", need["small"]),
                              ("small_recurrent", need["small"]), ("shard_state_accumulate", need["shard"]),
+                             ("shard_state_accumulate_tiles", need["shard"]),
                              ("shard_prefill", need["shard"])) if on]
 
     def step(evs):
@@ -342,7 +347,8 @@ def main():
             flush.fill_(1)
             timed("small_recurrent", lambda: la.prefill_recurrent(sq, sk, sv, so2, sS2))
         if need["shard"]:
-            timed("shard_state_accumulate", lambda: la.state_accumulate(hk, hv, hdS))
+            timed("shard_state_accumulate", lambda: la.state_accumulate_split(hk, hv, hdS, hws))
+            timed("shard_state_accumulate_tiles", lambda: la.state_accumulate(hk, hv, hdS2))
             timed("shard_prefill", lambda: la.prefill(hq, hk, hv, ho, hS0, SH["block"]))
 
     for _ in range(args.warmup):
@@ -456,6 +462,13 @@ def main():
             "workload": "one of 8 segments of the 1M-token sequence: B=1 H=64 N=131072 d=128, bf16",
             "state_accumulate_ms": avg["shard_state_accumulate"],
             "state_accumulate_GBps": state_accumulate_bytes(**SH) / (avg["shard_state_accumulate"] / 1e3) / 1e9,
+            "state_accumulate_kernel": "token-split (lin_attn_state_accumulate_split): one workgroup per "
+                                       "(sequence, chunk), chunk sums added in order",
+            "state_accumulate_tiles_ms": avg["shard_state_accumulate_tiles"],
+            "state_accumulate_tiles_GBps": state_accumulate_bytes(**SH)
+            / (avg["shard_state_accumulate_tiles"] / 1e3) / 1e9,
+            "state_accumulate_pct_of_read_only_stream_ceiling": 100 * state_accumulate_bytes(**SH)
+            / (avg["shard_state_accumulate"] / 1e3) / 1e9 / ceiling["read_only_GBps"],
             "prefill_nonzero_S0_ms": avg["shard_prefill"],
             "prefill_nonzero_S0_GBps": prefill_bytes(**SH) / (avg["shard_prefill"] / 1e3) / 1e9,
         },

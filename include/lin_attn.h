@@ -293,6 +293,36 @@ int lin_attn_state_accumulate(const void *k, const void *v, float *state,
                               lin_attn_dtype_t io_dtype, void *stream);
 
 /*
+ * The same state accumulation, cut along the tokens: each sequence's N
+ * tokens are split into chunks, one workgroup per (sequence, chunk) sums its
+ * chunk's K^T V over the whole d x d state, and the chunk sums are added to
+ * the state in chunk order (so the result is deterministic, and equal to the
+ * call above up to fp32 rounding).  Every K and V byte is then read once, as
+ * whole rows, by one workgroup; the call above reads each byte once per
+ * 64 x 64 tile row or column of the state that needs it.  The chunk sums
+ * other than the first go to a caller-provided workspace.
+ *
+ * lin_attn_state_accumulate_split_workspace returns the workspace bytes the
+ * call needs for these sizes (0 when a single chunk per sequence suffices,
+ * and for fp32 I/O, which runs the unsplit kernel), or a negative error code
+ * (LIN_ATTN_EINVAL, LIN_ATTN_EUNSUPPORTED) for arguments the call rejects.
+ *
+ * workspace       : device pointer, 16-byte aligned, at least that many
+ *                   bytes, owned by the caller, not aliasing k, v or state;
+ *                   may be NULL when 0 bytes are needed.  Its contents on
+ *                   entry are ignored and on return unspecified.
+ * workspace_bytes : its size; fewer bytes than needed give LIN_ATTN_EINVAL.
+ * Other arguments and errors as lin_attn_state_accumulate.  Calls that share
+ * a workspace must not run concurrently.
+ */
+int64_t lin_attn_state_accumulate_split_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
+                                                  lin_attn_dtype_t io_dtype);
+int lin_attn_state_accumulate_split(const void *k, const void *v, float *state,
+                                    int64_t B, int64_t H, int64_t N, int64_t d,
+                                    lin_attn_dtype_t io_dtype, void *workspace,
+                                    int64_t workspace_bytes, void *stream);
+
+/*
  * Backward pass (training): the gradients of L = sum_t <o_t, dout_t> +
  * <S_N, dstate> through the prefill above, for upstream gradients dout of
  * the outputs and dstate of the final state.  With the gradient reaching S_t,

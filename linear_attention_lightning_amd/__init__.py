@@ -26,9 +26,12 @@ from ._binding import (  # noqa: F401
     prefill_snapshots,
     snapshot_count,
     state_accumulate,
+    state_accumulate_split,
+    state_accumulate_split_workspace,
     strerror,
 )
 
 __all__ = ["prefill", "prefill_scaled", "backward", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
-           "prefill_snapshots", "snapshot_count", "state_accumulate", "strerror", "library", "LinAttnError",
+           "prefill_snapshots", "snapshot_count", "state_accumulate", "state_accumulate_split",
+           "state_accumulate_split_workspace", "strerror", "library", "LinAttnError",
            "F32", "BF16", "FP8_E4M3", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]

@@ -58,6 +58,10 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_decode_commit.restype = i32
             lib.lin_attn_state_accumulate.argtypes = [p, p, p, i64, i64, i64, i64, i32, p]
             lib.lin_attn_state_accumulate.restype = i32
+            lib.lin_attn_state_accumulate_split_workspace.argtypes = [i64, i64, i64, i64, i32]
+            lib.lin_attn_state_accumulate_split_workspace.restype = i64
+            lib.lin_attn_state_accumulate_split.argtypes = [p, p, p, i64, i64, i64, i64, i32, p, i64, p]
+            lib.lin_attn_state_accumulate_split.restype = i32
             lib.lin_attn_decode_verify_scaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
             lib.lin_attn_decode_verify_scaled.restype = i32
             lib.lin_attn_decode_commit_scaled.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
@@ -230,6 +234,48 @@ def state_accumulate(k, v, state, *, stream=None):
                                              _dtype_code(k), _stream(stream, k.device))
     if rc != OK:
         raise LinAttnError(rc, "lin_attn_state_accumulate")
+    return state
+
+
+def state_accumulate_split_workspace(B: int, H: int, N: int, d: int, dtype) -> int:
+    """Workspace bytes ``state_accumulate_split`` needs for these sizes and
+    the torch dtype of k and v (``lin_attn_state_accumulate_split_workspace``)."""
+    import torch
+    code = {torch.float32: F32, torch.bfloat16: BF16}.get(dtype)
+    if code is None:
+        raise LinAttnError(EUNSUPPORTED, "lin_attn_state_accumulate_split_workspace")
+    n = library().lin_attn_state_accumulate_split_workspace(B, H, N, d, code)
+    if n < 0:
+        raise LinAttnError(int(n), "lin_attn_state_accumulate_split_workspace")
+    return int(n)
+
+
+def state_accumulate_split(k, v, state, workspace=None, *, stream=None):
+    """state += K^T V with the tokens cut into chunks, one workgroup per
+    (sequence, chunk), chunk sums added in chunk order
+    (``lin_attn_state_accumulate_split``).
+
+    k, v: [B, H, N, d] bf16 or fp32 (same dtype); state: [B, H, d, d] fp32,
+    updated in place; workspace: a uint8 device tensor of at least
+    ``state_accumulate_split_workspace(...)`` bytes, or None to allocate one
+    here."""
+    import torch
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, N, d]")
+    B, H, N, d = k.shape
+    _check(v, "v", (B, H, N, d), k.dtype, k.device)
+    _check(k, "k", (B, H, N, d), k.dtype, k.device)
+    _check(state, "state", (B, H, d, d), torch.float32, k.device)
+    need = state_accumulate_split_workspace(B, H, N, d, k.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k.device)
+    if workspace.dtype != torch.uint8 or workspace.device != k.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the device of k")
+    rc = library().lin_attn_state_accumulate_split(k.data_ptr(), v.data_ptr(), state.data_ptr(), B, H, N, d,
+                                                   _dtype_code(k), workspace.data_ptr(), workspace.numel(),
+                                                   _stream(stream, k.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_state_accumulate_split")
     return state
 
 

@@ -110,5 +110,18 @@ struct StateDeltaF32Args {
   int64_t N;
 };
 hipError_t state_delta_f32_launch(StateDeltaF32Args a, int64_t BH, int d, hipStream_t stream);
+// Token-split state accumulation (bf16): chunk c of each sequence covers
+// tokens [c chunk_len, min((c+1) chunk_len, N)); chunk 0 adds into state,
+// chunks c >= 1 write their sums to partial[(c-1) BH + bh] ([d][d] fp32
+// each), which a second launch adds into state in chunk order.
+struct StateSplitArgs {
+  const unsigned short *k, *v;  // bf16 bit patterns, [BH][N][d]
+  float *state;                 // [BH][d][d]
+  float *partial;               // [(chunks-1) BH][d][d]
+  int64_t N, BH, chunks, chunk_len;
+};
+hipError_t state_split_launch(StateSplitArgs a, int d, hipStream_t stream);
+// chunks and chunk length (a multiple of 64) for BH sequences of N >= 1 tokens
+void state_split_plan(int64_t BH, int64_t N, int64_t *chunks, int64_t *chunk_len);
 
 }  // namespace lal

@@ -317,6 +317,54 @@ int lin_attn_state_accumulate(const void *k, const void *v, float *state, int64_
   return from_hip(lal::state_delta_f32_launch(a, BH, (int)d, s));
 }
 
+namespace {
+
+// Validation shared by the split state accumulation and its workspace query:
+// LIN_ATTN_OK with BH and the workspace bytes set, or an error code.
+int split_check(int64_t B, int64_t H, int64_t N, int64_t d, lin_attn_dtype_t io_dtype, int64_t *BH_out,
+                int64_t *chunks, int64_t *chunk_len, int64_t *ws_bytes) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return LIN_ATTN_EINVAL;
+  if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
+  int64_t BH, total;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &total) || !mul_ok(total, d, &total)) return LIN_ATTN_EINVAL;
+  *BH_out = BH;
+  *chunks = 1;
+  *chunk_len = N;
+  *ws_bytes = 0;
+  if (BH == 0 || N == 0 || io_dtype == LIN_ATTN_F32) return LIN_ATTN_OK;
+  lal::state_split_plan(BH, N, chunks, chunk_len);
+  int64_t groups;
+  if (!mul_ok(BH, *chunks, &groups) || groups > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  if (!mul_ok((*chunks - 1) * BH, d * d * 4, ws_bytes)) return LIN_ATTN_EINVAL;
+  return LIN_ATTN_OK;
+}
+
+}  // namespace
+
+int64_t lin_attn_state_accumulate_split_workspace(int64_t B, int64_t H, int64_t N, int64_t d,
+                                                  lin_attn_dtype_t io_dtype) {
+  int64_t BH, chunks, chunk_len, ws;
+  const int rc = split_check(B, H, N, d, io_dtype, &BH, &chunks, &chunk_len, &ws);
+  return rc == LIN_ATTN_OK ? ws : rc;
+}
+
+int lin_attn_state_accumulate_split(const void *k, const void *v, float *state, int64_t B, int64_t H, int64_t N,
+                                    int64_t d, lin_attn_dtype_t io_dtype, void *workspace, int64_t workspace_bytes,
+                                    void *stream) {
+  int64_t BH, chunks, chunk_len, ws;
+  const int rc = split_check(B, H, N, d, io_dtype, &BH, &chunks, &chunk_len, &ws);
+  if (rc != LIN_ATTN_OK) return rc;
+  if (workspace_bytes < ws) return LIN_ATTN_EINVAL;
+  if (BH == 0 || N == 0) return LIN_ATTN_OK;
+  if (io_dtype == LIN_ATTN_F32) return lin_attn_state_accumulate(k, v, state, B, H, N, d, io_dtype, stream);
+  if (!ok_ptr(k) || !ok_ptr(v) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  if (ws > 0 && !ok_ptr(workspace)) return LIN_ATTN_EINVAL;
+  lal::StateSplitArgs a{(const unsigned short *)k, (const unsigned short *)v, state, (float *)workspace,
+                        N, BH, chunks, chunk_len};
+  return from_hip(lal::state_split_launch(a, (int)d, (hipStream_t)stream));
+}
+
 const char *lin_attn_strerror(int code) {
   switch (code) {
     case LIN_ATTN_OK: return "success";

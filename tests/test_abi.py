@@ -294,3 +294,25 @@ def test_stream_probe_is_a_separate_library():
     assert lib.hbm_stream(FAKE, FAKE, 0, 3, 1, 0, 1, None) == 0  # nothing to do: no launch
     nm = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True, check=True)
     assert "hbm_stream" not in nm.stdout
+
+
+def test_split_accumulation_workspace_query_and_validation():
+    """The workspace query and the split accumulation reject what the call
+    rejects, before any launch; too small a workspace is EINVAL."""
+    lib = la.library()
+    q = lib.lin_attn_state_accumulate_split_workspace
+    assert q(1, 64, 131072, 128, la.BF16) == 3 * 64 * 128 * 128 * 4  # 4 chunks of 32768 tokens
+    assert q(4, 64, 32768, 128, la.BF16) == 0                         # 256 sequences: one chunk each
+    assert q(1, 2, 255, 128, la.BF16) == 0                            # too short to split
+    assert q(1, 2, 3000, 64, la.F32) == 0
+    assert q(1, 2, 100, 96, la.BF16) == la.EUNSUPPORTED
+    assert q(-1, 2, 100, 64, la.BF16) == la.EINVAL
+    assert q(1, 2, 100, 64, 7) == la.EUNSUPPORTED
+    f = lib.lin_attn_state_accumulate_split
+    need = q(1, 8, 4096, 128, la.BF16)
+    assert need > 0
+    assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 128, la.BF16, FAKE, need - 1, None) == la.EINVAL
+    assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 128, la.BF16, None, need, None) == la.EINVAL
+    assert f(FAKE, FAKE, MISALIGNED, 1, 8, 4096, 128, la.BF16, FAKE, need, None) == la.EINVAL
+    assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 96, la.BF16, FAKE, need, None) == la.EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, 8, 0, 128, la.BF16, None, 0, None) == la.OK  # nothing to do
