@@ -307,6 +307,11 @@ def main():
         la.state_accumulate(hk, hv, hS0)
         hdS = torch.zeros_like(hS0)
         hdS2 = torch.zeros_like(hS0)
+        hS0b = hS0.clone()
+        ho2 = torch.empty_like(hq)
+        hpws = torch.empty(max(16, la.prefill_seqsplit_workspace(SH["B"], SH["H"], SH["N"], SH["d"], SH["block"],
+                                                                 torch.bfloat16)),
+                           dtype=torch.uint8, device=dev)
         hws = torch.empty(max(16, la.state_accumulate_split_workspace(SH["B"], SH["H"], SH["N"], SH["d"],
                                                                       torch.bfloat16)),
                           dtype=torch.uint8, device=dev)
@@ -321,6 +326,7 @@ def main():
                              ("commit", need["decode"]), ("small_chunked", need["small"]),
                              ("small_recurrent", need["small"]), ("shard_state_accumulate", need["shard"]),
                              ("shard_state_accumulate_tiles", need["shard"]),
+                             ("shard_prefill_seqsplit", need["shard"]),
                              ("shard_prefill", need["shard"])) if on]
 
     def step(evs):
@@ -350,6 +356,7 @@ def main():
             timed("shard_state_accumulate", lambda: la.state_accumulate_split(hk, hv, hdS, hws))
             timed("shard_state_accumulate_tiles", lambda: la.state_accumulate(hk, hv, hdS2))
             timed("shard_prefill", lambda: la.prefill(hq, hk, hv, ho, hS0, SH["block"]))
+            timed("shard_prefill_seqsplit", lambda: la.prefill_seqsplit(hq, hk, hv, ho2, hS0b, SH["block"], hpws))
 
     for _ in range(args.warmup):
         step(None)
@@ -471,6 +478,12 @@ def main():
             / (avg["shard_state_accumulate"] / 1e3) / 1e9 / ceiling["read_only_GBps"],
             "prefill_nonzero_S0_ms": avg["shard_prefill"],
             "prefill_nonzero_S0_GBps": prefill_bytes(**SH) / (avg["shard_prefill"] / 1e3) / 1e9,
+            "prefill_nonzero_S0_kernel": "lin_attn_prefill: 64 sequences, value columns split 4 ways",
+            "prefill_seqsplit_nonzero_S0_ms": avg["shard_prefill_seqsplit"],
+            "prefill_seqsplit_nonzero_S0_tokens_per_s": SH["B"] * SH["N"] / (avg["shard_prefill_seqsplit"] / 1e3),
+            "prefill_seqsplit_algorithmic_GBps": prefill_bytes(**SH) / (avg["shard_prefill_seqsplit"] / 1e3) / 1e9,
+            "prefill_seqsplit_kernel": "lin_attn_prefill_seqsplit: 4 parts per sequence, part states from the "
+                                       "token-split K^T V of the parts before, 256 part prefills",
         },
         "roofline": {
             "bound": "hbm",

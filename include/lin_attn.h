@@ -323,6 +323,37 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state,
                                     int64_t workspace_bytes, void *stream);
 
 /*
+ * Prefill cut along the tokens, for few sequences: the same outputs and
+ * final state as lin_attn_prefill (up to fp32 rounding of the carried
+ * state), computed as follows.  Each sequence's N tokens are cut into P equal
+ * parts so that B*H*P is about 256 (one chunked-prefill workgroup per compute
+ * unit; parts of at least 2048 tokens, P a power of two dividing N).  The
+ * K^T V of the first P-1 parts is summed by the token-split accumulation
+ * (into the workspace); each part's initial state is S_0 plus the sums of the
+ * parts before it, added in part order (the associativity equation of
+ * [ZENN], section "線形アテンションの数学的基礎": the state after a
+ * concatenation is the sum of the segments' K^T V); the parts then run as
+ * B*H*P independent prefills, and the last part's final state is written to
+ * state.  This reads K and V once more for (P-1)/P of the tokens and in
+ * exchange fills the GPU where B*H alone would leave compute units idle.
+ * When P = 1 (enough sequences, short or indivisible N, or fp32 I/O) the
+ * call is lin_attn_prefill and needs no workspace.
+ *
+ * lin_attn_prefill_seqsplit_workspace returns the workspace bytes the call
+ * needs, (2P - 1 + (P-1)(S-1)) * B*H * d*d * 4 for S <= 4 accumulation chunks
+ * per part (0 when P = 1), or a negative error code for arguments the call
+ * rejects.
+ * workspace, workspace_bytes: as lin_attn_state_accumulate_split.  Other
+ * arguments, layouts and errors as lin_attn_prefill.
+ */
+int64_t lin_attn_prefill_seqsplit_workspace(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                                            lin_attn_dtype_t io_dtype);
+int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void *o, float *state,
+                              int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                              lin_attn_dtype_t io_dtype, void *workspace, int64_t workspace_bytes,
+                              void *stream);
+
+/*
  * Backward pass (training): the gradients of L = sum_t <o_t, dout_t> +
  * <S_N, dstate> through the prefill above, for upstream gradients dout of
  * the outputs and dstate of the final state.  With the gradient reaching S_t,

@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     prefill,
     prefill_recurrent,
     prefill_scaled,
+    prefill_seqsplit,
+    prefill_seqsplit_workspace,
     prefill_snapshots,
     snapshot_count,
     state_accumulate,
@@ -31,7 +33,7 @@ from ._binding import (  # noqa: F401
     strerror,
 )
 
-__all__ = ["prefill", "prefill_scaled", "backward", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
+__all__ = ["prefill", "prefill_scaled", "prefill_seqsplit", "prefill_seqsplit_workspace", "backward", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
            "prefill_snapshots", "snapshot_count", "state_accumulate", "state_accumulate_split",
            "state_accumulate_split_workspace", "strerror", "library", "LinAttnError",
            "F32", "BF16", "FP8_E4M3", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]

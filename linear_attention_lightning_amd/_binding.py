@@ -62,6 +62,10 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_state_accumulate_split_workspace.restype = i64
             lib.lin_attn_state_accumulate_split.argtypes = [p, p, p, i64, i64, i64, i64, i32, p, i64, p]
             lib.lin_attn_state_accumulate_split.restype = i32
+            lib.lin_attn_prefill_seqsplit_workspace.argtypes = [i64, i64, i64, i64, i64, i32]
+            lib.lin_attn_prefill_seqsplit_workspace.restype = i64
+            lib.lin_attn_prefill_seqsplit.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, p, i64, p]
+            lib.lin_attn_prefill_seqsplit.restype = i32
             lib.lin_attn_decode_verify_scaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
             lib.lin_attn_decode_verify_scaled.restype = i32
             lib.lin_attn_decode_commit_scaled.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
@@ -277,6 +281,45 @@ def state_accumulate_split(k, v, state, workspace=None, *, stream=None):
     if rc != OK:
         raise LinAttnError(rc, "lin_attn_state_accumulate_split")
     return state
+
+
+def prefill_seqsplit_workspace(B: int, H: int, N: int, d: int, block: int, dtype) -> int:
+    """Workspace bytes ``prefill_seqsplit`` needs (``lin_attn_prefill_seqsplit_workspace``)."""
+    import torch
+    code = {torch.float32: F32, torch.bfloat16: BF16}.get(dtype)
+    if code is None:
+        raise LinAttnError(EUNSUPPORTED, "lin_attn_prefill_seqsplit_workspace")
+    n = library().lin_attn_prefill_seqsplit_workspace(B, H, N, d, int(block), code)
+    if n < 0:
+        raise LinAttnError(int(n), "lin_attn_prefill_seqsplit_workspace")
+    return int(n)
+
+
+def prefill_seqsplit(q, k, v, o, state, block: int = 128, workspace=None, *, stream=None):
+    """Chunked prefill with each sequence cut into parts along the tokens
+    (``lin_attn_prefill_seqsplit``): the parts' initial states come from the
+    K^T V of the parts before them, and the parts run as independent
+    sequences.  Same arguments as ``prefill``; workspace: a uint8 device
+    tensor of at least ``prefill_seqsplit_workspace(...)`` bytes, or None to
+    allocate one here."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, n, (B, H, N, d), q.dtype, q.device)
+    _check(state, "state", (B, H, d, d), torch.float32, q.device)
+    need = prefill_seqsplit_workspace(B, H, N, d, block, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the device of q")
+    rc = library().lin_attn_prefill_seqsplit(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                             state.data_ptr(), B, H, N, d, int(block), _dtype_code(q),
+                                             workspace.data_ptr(), workspace.numel(), _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_prefill_seqsplit")
+    return o
 
 
 def snapshot_count(N: int, block: int, every: int) -> int:

@@ -119,9 +119,21 @@ struct StateSplitArgs {
   float *state;                 // [BH][d][d]
   float *partial;               // [(chunks-1) BH][d][d]
   int64_t N, BH, chunks, chunk_len;
+  // non-zero: every chunk c starts from zero and writes partial[c BH + bh]
+  // (partial then holds chunks BH states; state is not touched)
+  int all_partial;
 };
 hipError_t state_split_launch(StateSplitArgs a, int d, hipStream_t stream);
 // chunks and chunk length (a multiple of 64) for BH sequences of N >= 1 tokens
 void state_split_plan(int64_t BH, int64_t N, int64_t *chunks, int64_t *chunk_len);
+
+// Initial states of the P parts of each sequence for a prefill cut along the
+// tokens: starts[bh P + p] = state[bh] + sum over chunks c < p S of
+// partial[c BH + bh] (in chunk order), for p = 0 .. P-1; [d][d] fp32 each.
+hipError_t state_part_starts_launch(const float *state, const float *partial, float *starts, int64_t BH,
+                                    int64_t P, int64_t S, int d, hipStream_t stream);
+// state[bh] = starts[bh P + P - 1] (the final state of each sequence's last part)
+hipError_t state_take_last_launch(const float *starts, float *state, int64_t BH, int64_t P, int d,
+                                  hipStream_t stream);
 
 }  // namespace lal

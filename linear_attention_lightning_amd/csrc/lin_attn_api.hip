@@ -361,8 +361,82 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state, 
   if (!ok_ptr(k) || !ok_ptr(v) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
   if (ws > 0 && !ok_ptr(workspace)) return LIN_ATTN_EINVAL;
   lal::StateSplitArgs a{(const unsigned short *)k, (const unsigned short *)v, state, (float *)workspace,
-                        N, BH, chunks, chunk_len};
+                        N, BH, chunks, chunk_len, 0};
   return from_hip(lal::state_split_launch(a, (int)d, (hipStream_t)stream));
+}
+
+namespace {
+
+// Prefill cut along the tokens: P parts per sequence (B*H*P about 256, parts of
+// at least 2048 tokens, P a power of two dividing N); the K^T V of the first
+// P-1 parts is summed in chunks of L/S tokens (S a power of two <= 4 dividing
+// L, chunks of at least 1024 tokens).  Workspace: (P-1) S BH partial states,
+// then BH P part states.
+struct SeqSplitPlan {
+  int64_t BH, P, L, S, ws_bytes;
+};
+
+int seqsplit_check(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
+                   SeqSplitPlan *pl) {
+  if (B < 0 || H < 0 || N < 0 || d < 0 || block < 0) return LIN_ATTN_EINVAL;
+  if (io_dtype != LIN_ATTN_F32 && io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
+  const int max_block = io_dtype == LIN_ATTN_BF16 ? lal::prefill_bf16_max_block((int)d)
+                                                  : lal::prefill_f32_max_block((int)d);
+  if (block < 16 || block > max_block || block % 16 != 0) return LIN_ATTN_EUNSUPPORTED;
+  int64_t BH, total;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &total) || !mul_ok(total, d, &total)) return LIN_ATTN_EINVAL;
+  pl->BH = BH;
+  pl->P = 1;
+  pl->S = 1;
+  pl->ws_bytes = 0;
+  if (io_dtype == LIN_ATTN_BF16 && BH > 0 && N > 0) {
+    while (BH * pl->P * 2 <= 256 && N % (pl->P * 2) == 0 && N / (pl->P * 2) >= 2048) pl->P *= 2;
+  }
+  pl->L = pl->P > 0 ? N / pl->P : N;
+  if (pl->P > 1) {
+    while (pl->S < 4 && pl->L % (pl->S * 2) == 0 && pl->L / (pl->S * 2) >= 1024) pl->S *= 2;
+    const int64_t states = (pl->P - 1) * pl->S * BH + BH * pl->P;
+    if (!mul_ok(states, d * d * 4, &pl->ws_bytes)) return LIN_ATTN_EINVAL;
+  }
+  return LIN_ATTN_OK;
+}
+
+}  // namespace
+
+int64_t lin_attn_prefill_seqsplit_workspace(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                                            lin_attn_dtype_t io_dtype) {
+  SeqSplitPlan pl;
+  const int rc = seqsplit_check(B, H, N, d, block, io_dtype, &pl);
+  return rc == LIN_ATTN_OK ? pl.ws_bytes : rc;
+}
+
+int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void *o, float *state, int64_t B,
+                              int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
+                              void *workspace, int64_t workspace_bytes, void *stream) {
+  SeqSplitPlan pl;
+  int rc = seqsplit_check(B, H, N, d, block, io_dtype, &pl);
+  if (rc != LIN_ATTN_OK) return rc;
+  if (workspace_bytes < pl.ws_bytes) return LIN_ATTN_EINVAL;
+  if (pl.P == 1) return prefill_impl(q, k, v, o, state, nullptr, 0, B, H, N, d, block, io_dtype, 0, stream);
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state) || !ok_ptr(workspace))
+    return LIN_ATTN_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  float *partial = (float *)workspace;
+  float *starts = partial + (size_t)(pl.P - 1) * pl.S * pl.BH * d * d;
+  // 1. K^T V of the first P-1 parts, in (P-1) S chunks per sequence
+  lal::StateSplitArgs a{(const unsigned short *)k, (const unsigned short *)v, state, partial,
+                        N, pl.BH, (pl.P - 1) * pl.S, pl.L / pl.S, 1};
+  rc = from_hip(lal::state_split_launch(a, (int)d, s));
+  if (rc != LIN_ATTN_OK) return rc;
+  // 2. each part's initial state: S_0 plus the sums of the parts before it
+  rc = from_hip(lal::state_part_starts_launch(state, partial, starts, pl.BH, pl.P, pl.S, (int)d, s));
+  if (rc != LIN_ATTN_OK) return rc;
+  // 3. the parts as B*H*P independent sequences of L tokens (contiguous in memory)
+  rc = prefill_impl(q, k, v, o, starts, nullptr, 0, pl.BH * pl.P, 1, pl.L, d, block, io_dtype, 0, stream);
+  if (rc != LIN_ATTN_OK) return rc;
+  // 4. the final state is the last part's
+  return from_hip(lal::state_take_last_launch(starts, state, pl.BH, pl.P, (int)d, s));
 }
 
 const char *lin_attn_strerror(int code) {

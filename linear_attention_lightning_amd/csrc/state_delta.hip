@@ -285,7 +285,9 @@ __global__ __launch_bounds__(kThreadsSD) void state_split_bf16_kernel(StateSplit
   const int64_t len = (N - t_begin < a.chunk_len ? N - t_begin : a.chunk_len);  // >= 1 by the host plan
   const u16 *kh = a.k + ((size_t)bh * (size_t)N + (size_t)t_begin) * D;
   const u16 *vh = a.v + ((size_t)bh * (size_t)N + (size_t)t_begin) * D;
-  float *out = c == 0 ? a.state + (size_t)bh * D * D : a.partial + ((size_t)(c - 1) * a.BH + (size_t)bh) * D * D;
+  const bool from_state = c == 0 && !a.all_partial;
+  float *out = from_state ? a.state + (size_t)bh * D * D
+                          : a.partial + ((size_t)(a.all_partial ? c : c - 1) * a.BH + (size_t)bh) * D * D;
 
   // wave w owns S columns 16 NJW w .. + 16 NJW - 1, all rows; acc[x][y] holds
   // rows 16x + 4g + e, column 16 (NJW w + y) + lr
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(kThreadsSD) void state_split_bf16_kernel(StateSplit
   for (int x = 0; x < NI; ++x)
 #pragma unroll
     for (int y = 0; y < NJW; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (c == 0) {
+  if (from_state) {
 #pragma unroll
     for (int x = 0; x < NI; ++x)
 #pragma unroll
@@ -390,11 +392,30 @@ __global__ __launch_bounds__(256) void state_split_reduce_kernel(StateSplitArgs 
   *st = acc;
 }
 
+__global__ __launch_bounds__(256) void part_starts_kernel(const float *state, const float *partial, float *starts,
+                                                         int64_t BH, int64_t P, int64_t S, int64_t per_head4) {
+  const int64_t bh = blockIdx.x / (per_head4 / 256);
+  const int64_t i = (int64_t)(blockIdx.x % (per_head4 / 256)) * 256 + threadIdx.x;  // float4 index
+  f32x4 acc = ((const f32x4 *)state)[bh * per_head4 + i];
+  ((f32x4 *)starts)[(bh * P) * per_head4 + i] = acc;
+  for (int64_t p = 1; p < P; ++p) {
+    for (int64_t c = (p - 1) * S; c < p * S; ++c) acc += ((const f32x4 *)partial)[(c * BH + bh) * per_head4 + i];
+    ((f32x4 *)starts)[(bh * P + p) * per_head4 + i] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void take_last_kernel(const float *starts, float *state, int64_t P,
+                                                       int64_t per_head4) {
+  const int64_t bh = blockIdx.x / (per_head4 / 256);
+  const int64_t i = (int64_t)(blockIdx.x % (per_head4 / 256)) * 256 + threadIdx.x;
+  ((f32x4 *)state)[bh * per_head4 + i] = ((const f32x4 *)starts)[(bh * P + P - 1) * per_head4 + i];
+}
+
 template <int D>
 hipError_t launch_split(StateSplitArgs a, hipStream_t stream) {
   hipLaunchKernelGGL(state_split_bf16_kernel<D>, dim3((unsigned)(a.BH * a.chunks)), dim3(kThreadsSD), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.chunks == 1) return e;
+  if (e != hipSuccess || a.chunks == 1 || a.all_partial) return e;
   hipLaunchKernelGGL(state_split_reduce_kernel<D>, dim3((unsigned)(a.BH * (D * D / 1024))), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -427,6 +448,22 @@ hipError_t state_split_launch(StateSplitArgs a, int d, hipStream_t stream) {
   if (d == 128) return launch_split<128>(a, stream);
   if (d == 64) return launch_split<64>(a, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t state_part_starts_launch(const float *state, const float *partial, float *starts, int64_t BH,
+                                    int64_t P, int64_t S, int d, hipStream_t stream) {
+  const int64_t per_head4 = (int64_t)d * d / 4;  // 4096 or 1024: a multiple of 256
+  hipLaunchKernelGGL(part_starts_kernel, dim3((unsigned)(BH * (per_head4 / 256))), dim3(256), 0, stream, state,
+                     partial, starts, BH, P, S, per_head4);
+  return hipGetLastError();
+}
+
+hipError_t state_take_last_launch(const float *starts, float *state, int64_t BH, int64_t P, int d,
+                                  hipStream_t stream) {
+  const int64_t per_head4 = (int64_t)d * d / 4;
+  hipLaunchKernelGGL(take_last_kernel, dim3((unsigned)(BH * (per_head4 / 256))), dim3(256), 0, stream, starts, state,
+                     P, per_head4);
+  return hipGetLastError();
 }
 
 void state_split_plan(int64_t BH, int64_t N, int64_t *chunks, int64_t *chunk_len) {

@@ -316,3 +316,24 @@ def test_split_accumulation_workspace_query_and_validation():
     assert f(FAKE, FAKE, MISALIGNED, 1, 8, 4096, 128, la.BF16, FAKE, need, None) == la.EINVAL
     assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 96, la.BF16, FAKE, need, None) == la.EUNSUPPORTED
     assert f(FAKE, FAKE, FAKE, 1, 8, 0, 128, la.BF16, None, 0, None) == la.OK  # nothing to do
+
+
+def test_seqsplit_workspace_query_and_validation():
+    lib = la.library()
+    q = lib.lin_attn_prefill_seqsplit_workspace
+    # 64 sequences of 131072 tokens: 4 parts of 32768, 4 accumulation chunks each:
+    # 3 * 4 * 64 partial states + 64 * 4 part states, 64 KiB each
+    assert q(1, 64, 131072, 128, 128, la.BF16) == (3 * 4 * 64 + 64 * 4) * 128 * 128 * 4
+    assert q(4, 64, 32768, 128, 128, la.BF16) == 0
+    assert q(1, 8, 4095, 128, 128, la.BF16) == 0       # indivisible / short: no cut
+    assert q(1, 8, 4096, 128, 64, la.F32) == 0         # fp32 I/O: the uncut prefill
+    assert q(1, 8, 4096, 128, 100, la.BF16) == la.EUNSUPPORTED
+    assert q(1, 8, 4096, 96, 128, la.BF16) == la.EUNSUPPORTED
+    assert q(1, -8, 4096, 128, 128, la.BF16) == la.EINVAL
+    f = lib.lin_attn_prefill_seqsplit
+    need = q(1, 8, 8192, 128, 128, la.BF16)
+    assert need > 0
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 128, 128, la.BF16)
+    assert f(*args, FAKE, need - 1, None) == la.EINVAL
+    assert f(*args, None, need, None) == la.EINVAL
+    assert f(FAKE, FAKE, FAKE, MISALIGNED, FAKE, 1, 8, 8192, 128, 128, la.BF16, FAKE, need, None) == la.EINVAL
