@@ -21,6 +21,9 @@ heads) over the timed steps.  Prints ONE JSON line.
 
 ``--only crossover`` sweeps the chunked and the token-by-token prefill over
 N = 256 ... 32768 at the crossover shape (see crossover_sweep).
+``--only long`` times the long-context prefill (B=1, H=64, N=1048576, d=128,
+block 128; 16 GiB per tensor) with the value-column split and with the
+sequence split (see long_context).
 ``--only ceiling`` measures the HBM bandwidth a plain streaming kernel
 reaches for the path's read:write byte mixes (see hbm_ceiling); the default
 run includes it.
@@ -158,6 +161,50 @@ def cpu_baseline(heads: int = 64, min_seconds: float = 10.0, max_passes: int = 6
     }
 
 
+LONG = dict(B=1, H=64, N=1 << 20, d=128, block=128)
+
+
+def long_context(la, synth, torch, steps: int = 5):
+    """The 1M-token prefill over 64 heads from a zero state: lin_attn_prefill
+    (64 sequences; the value columns split 4 ways to fill the GPU) against
+    lin_attn_prefill_seqsplit (each sequence cut into 4 parts whose initial
+    states come from the token-split K^T V of the parts before).  HIP events
+    on the launch stream, `steps` timed launches after one untimed one; the
+    state is reset outside the timed region."""
+    L = LONG
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    q, k, v = synth.prefill_inputs_device(8, L["B"], L["H"], L["N"], L["d"])
+    o = torch.empty_like(q)
+    S = torch.zeros((L["B"], L["H"], L["d"], L["d"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, la.prefill_seqsplit_workspace(L["B"], L["H"], L["N"], L["d"], L["block"],
+                                                           torch.bfloat16)), dtype=torch.uint8, device=dev)
+    res = {}
+    for name, fn in (("value_split", lambda: la.prefill(q, k, v, o, S, L["block"])),
+                     ("seqsplit", lambda: la.prefill_seqsplit(q, k, v, o, S, L["block"], ws))):
+        ms = []
+        for i in range(steps + 1):
+            S.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i > 0:
+                ms.append(e0.elapsed_time(e1))
+        res[name] = sum(ms) / len(ms)
+    tokens = L["B"] * L["N"]
+    nbytes = prefill_bytes(**L)
+    return {"metric": "long-context prefill time (ms per launch)",
+            "config": {"workload": "B=1 H=64 N=1048576 d=128 block=128, bf16 q/k/v/o, fp32 state from zero"},
+            "value_split_ms": res["value_split"], "seqsplit_ms": res["seqsplit"],
+            "seqsplit_tokens_per_s": tokens / (res["seqsplit"] / 1e3),
+            "seqsplit_algorithmic_GBps": nbytes / (res["seqsplit"] / 1e3) / 1e9,
+            "value_split_tokens_per_s": tokens / (res["value_split"] / 1e3),
+            "algorithmic_bytes": nbytes,
+            "seqsplit_workspace_bytes": ws.numel()}
+
+
 def hbm_ceiling(torch, reps: int = 5):
     """Practical HBM ceiling of each traffic mix of the path, from a plain
     streaming kernel (csrc/hbm_stream.hip, its own library): 16-byte
@@ -212,7 +259,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy", "drift", "crossover",
-                                       "ceiling"],
+                                       "ceiling", "long"],
                     help="run one kernel only (for counter collection); prints timings, no JSON")
     args = ap.parse_args()
 
@@ -240,6 +287,9 @@ def main():
         print(json.dumps(crossover_sweep(la, synth, torch, steps=args.steps)))
         return
 
+    if args.only == "long":
+        print(json.dumps(long_context(la, synth, torch)))
+        return
     if args.only == "ceiling":
         print(json.dumps(hbm_ceiling(torch)))
         return

@@ -3,10 +3,10 @@
 // (winzheng.jp), section "推論システム統合の課題", names for linear attention):
 //
 //  verify:  o_t = q_t^T S_t for t = 0 .. T-1, S_t = S + sum_{s <= t} k_s v_s^T,
-//           computed as  q_t^T S  +  sum_{s <= t} (q_t . k_s) v_s  without
-//           writing the state (the recurrence of "MiniMax-M1で理解する"
+//           without writing the state (the recurrence of "MiniMax-M1で理解する"
 //           (zenn.dev/liushuzhi), section "線形アテンションの数学的基礎",
-//           unrolled over the drafts);
+//           unrolled over the drafts): each state row is read once and
+//           carried through the drafts in registers;
 //  commit:  S <- S + sum_{t < a} k_t v_t^T for the a drafts accepted by the
 //           sequence (a = 0 leaves S as it was: the rollback).
 //
@@ -15,7 +15,8 @@
 // T.  Layout as in the one-token decode: one wavefront per (batch, head),
 // each lane owns 4 columns of the rows it walks (16-byte fp32 or 8-byte bf16
 // state accesses); q and k of the drafts are staged in LDS (transposed, so a
-// state row's T multipliers are contiguous).
+// state row's T multipliers are contiguous), and each lane keeps its columns
+// of the drafts' v in registers.
 //
 // commit applies, per state element, the same fused multiply-adds in the
 // same order as T one-token decode steps; with an fp32 state the result is
@@ -79,7 +80,11 @@ __device__ __forceinline__ void st_state4(void *row, int cg, const float (&s)[4]
   }
 }
 
-template <int D, bool IO_BF16, int ST>
+// verify, with TM >= T drafts of room.  Per state row i each lane carries
+// c = S[i][cols] + sum_{s <= t} k_s[i] v_s[cols] through the drafts t and
+// adds q_t[i] c to output t: o_t = q_t^T S_t term by term, one pass over the
+// state and no separate q_t . k_s products.
+template <int D, bool IO_BF16, int ST, int TM>
 __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   constexpr int ES = ST == kStF32 ? 4 : ST == kStBF16 ? 2 : 1;
   constexpr int LPR = D / 4;    // lanes per state row (4 columns each)
@@ -87,38 +92,77 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   constexpr int RPL = D / RP;   // rows per lane
   constexpr int U = 8;          // rows in flight per lane
   static_assert(RPL % U == 0, "row unroll");
+  static_assert(TM % 4 == 0, "LDS rows of whole float4s");
+  constexpr int EPC = IO_BF16 ? 8 : 4;           // elements per 16-byte piece of q or k
+  constexpr int NP = (D * TM / EPC + 63) / 64;   // pieces per lane, at most
   extern __shared__ float lds[];
   const int T = a.T;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  float *qT = lds + (size_t)wave * (2 * D * T + kTMax * kTMax);  // qT[i * T + t]
-  float *kT = qT + D * T;                                       // kT[i * T + s]
-  float *P = kT + D * T;                                        // P[t * kTMax + s]
+  float *qT = lds + (size_t)wave * 2 * D * TM;  // qT[i * TM + t]
+  float *kT = qT + D * TM;                      // kT[i * TM + t]
   const int64_t h = (int64_t)blockIdx.x * kWV + wave;
   const bool valid = h < a.BH;
+  const int cg = lane % LPR, rph = lane / LPR;
+
+  float vr[TM][4];  // this lane's 4 columns of every draft's v
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vr[t][e] = 0.f;
   if (valid) {
-    for (int x = lane; x < D * T; x += 64) {
-      const int t = x / D, i = x % D;
-      qT[i * T + t] = ld_io<IO_BF16>(a.q, ((size_t)h * T + t) * D + i);
-      kT[i * T + t] = ld_io<IO_BF16>(a.k, ((size_t)h * T + t) * D + i);
+    // q and k of the drafts, transposed into LDS: every 16-byte load is
+    // issued before the first store (the stores wait on them)
+    const int npieces = D * T / EPC;
+    const char *qb = (const char *)a.q + (size_t)h * T * D * (IO_BF16 ? 2 : 4);
+    const char *kb = (const char *)a.k + (size_t)h * T * D * (IO_BF16 ? 2 : 4);
+    u32x4 qp[NP], kp[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int c = lane + 64 * j;
+      if (c < npieces) {
+        qp[j] = *(const u32x4 *)(qb + (size_t)c * 16);
+        kp[j] = *(const u32x4 *)(kb + (size_t)c * 16);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < T) {
+        const size_t base = ((size_t)h * T + t) * D + 4 * cg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[t][e] = ld_io<IO_BF16>(a.v, base + e);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int c = lane + 64 * j;
+      if (c < npieces) {
+        const int t = c * EPC / D, i0 = c * EPC % D;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          float qv, kv;
+          if constexpr (IO_BF16) {
+            const uint32_t wq = qp[j][e / 2], wk = kp[j][e / 2];
+            qv = __uint_as_float(e & 1 ? wq & 0xffff0000u : wq << 16);
+            kv = __uint_as_float(e & 1 ? wk & 0xffff0000u : wk << 16);
+          } else {
+            qv = __uint_as_float(qp[j][e]);
+            kv = __uint_as_float(kp[j][e]);
+          }
+          qT[(i0 + e) * TM + t] = qv;
+          kT[(i0 + e) * TM + t] = kv;
+        }
+      }
     }
   }
   __syncthreads();
   if (!valid) return;
 
-  // P[t][s] = q_t . k_s for s <= t
-  for (int x = lane; x < T * T; x += 64) {
-    const int t = x / T, s = x % T;
-    float p = 0.f;
-    if (s <= t)
-      for (int i = 0; i < D; ++i) p = fmaf(qT[i * T + t], kT[i * T + s], p);
-    P[t * kTMax + s] = p;
-  }
-
-  const int cg = lane % LPR, rph = lane / LPR;
-  float acc[kTMax][4];
+  // narrow states are read in stored units: the state value is code * scale
+  const float sc = (ST != kStF32 && a.scale) ? a.scale[h] : 1.f;
+  float acc[TM][4];
 #pragma unroll
-  for (int t = 0; t < kTMax; ++t)
+  for (int t = 0; t < TM; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
 
@@ -129,13 +173,29 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
     for (int u = 0; u < U; ++u) ld_state4<ST>(Sh + (size_t)(rph + RP * (m0 + u)) * D * ES, cg, s[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float *qi = qT + (rph + RP * (m0 + u)) * T;
+      const int i = rph + RP * (m0 + u);
+      float qv[TM], kv[TM];
 #pragma unroll
-      for (int t = 0; t < kTMax; ++t) {
+      for (int t4 = 0; t4 < TM; t4 += 4) {
+        const f32x4 q4 = *(const f32x4 *)(qT + i * TM + t4);
+        const f32x4 k4 = *(const f32x4 *)(kT + i * TM + t4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qv[t4 + e] = q4[e];
+          kv[t4 + e] = k4[e];
+        }
+      }
+      float c[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = ST == kStF32 ? s[u][e] : s[u][e] * sc;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
         if (t < T) {
-          const float qv = qi[t];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(qv, s[u][e], acc[t][e]);
+          for (int e = 0; e < 4; ++e) {
+            c[e] = fmaf(kv[t], vr[t][e], c[e]);
+            acc[t][e] = fmaf(qv[t], c[e], acc[t][e]);
+          }
         }
       }
     }
@@ -144,50 +204,22 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
-    for (int t = 0; t < kTMax; ++t)
+    for (int t = 0; t < TM; ++t)
       if (t < T)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[t][e] += __shfl_xor(acc[t][e], off, 64);
-  if constexpr (ST != kStF32) {
-    // the state part was read in stored units
-    const float sc = a.scale ? a.scale[h] : 1.f;
-#pragma unroll
-    for (int t = 0; t < kTMax; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] *= sc;
-  }
-  // P was written by other lanes of this wavefront: its LDS stores precede
-  // the reads below in the wavefront's in-order LDS queue once drained
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
   if (rph == 0) {
-    // within the drafts: o_t += sum_{s <= t} P[t][s] v_s
 #pragma unroll
-    for (int s = 0; s < kTMax; ++s) {
-      if (s < T) {
-        float vs[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vs[e] = ld_io<IO_BF16>(a.v, ((size_t)h * T + s) * D + 4 * cg + e);
-#pragma unroll
-        for (int t = 0; t < kTMax; ++t) {
-          if (t >= s && t < T) {
-            const float p = P[t * kTMax + s];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(p, vs[e], acc[t][e]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kTMax; ++t) {
+    for (int t = 0; t < TM; ++t) {
       if (t < T) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const size_t oi = ((size_t)h * T + t) * D + 4 * cg + e;
-          if constexpr (IO_BF16)
-            ((u16 *)a.o)[oi] = f32_to_bf16_bits(acc[t][e]);
-          else
-            ((float *)a.o)[oi] = acc[t][e];
+        const size_t oi = ((size_t)h * T + t) * D + 4 * cg;
+        if constexpr (IO_BF16) {
+          const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[t][0]) | ((uint32_t)f32_to_bf16_bits(acc[t][1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc[t][2]) | ((uint32_t)f32_to_bf16_bits(acc[t][3]) << 16);
+          *(u32x2 *)((u16 *)a.o + oi) = u32x2{lo, hi};
+        } else {
+          *(f32x4 *)((float *)a.o + oi) = f32x4{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
         }
       }
     }
@@ -262,8 +294,17 @@ hipError_t go(const DecodeMultiArgs &a, bool commit, hipStream_t stream) {
     hipLaunchKernelGGL((commit_kernel<D, IO, ST>), dim3((unsigned)grid), dim3(64 * kW), lds, stream, a);
   } else {
     const int64_t grid = (a.BH + kWV - 1) / kWV;
-    const size_t lds = (size_t)kWV * (2 * D * a.T + kTMax * kTMax) * sizeof(float);  // <= 34 KiB
-    hipLaunchKernelGGL((verify_kernel<D, IO, ST>), dim3((unsigned)grid), dim3(64 * kWV), lds, stream, a);
+    // room for TM = 4, 8 or 16 drafts (registers and LDS scale with it)
+    if (a.T <= 4) {
+      const size_t lds = (size_t)kWV * 2 * D * 4 * sizeof(float);
+      hipLaunchKernelGGL((verify_kernel<D, IO, ST, 4>), dim3((unsigned)grid), dim3(64 * kWV), lds, stream, a);
+    } else if (a.T <= 8) {
+      const size_t lds = (size_t)kWV * 2 * D * 8 * sizeof(float);
+      hipLaunchKernelGGL((verify_kernel<D, IO, ST, 8>), dim3((unsigned)grid), dim3(64 * kWV), lds, stream, a);
+    } else {
+      const size_t lds = (size_t)kWV * 2 * D * 16 * sizeof(float);  // 32 KiB at d = 128
+      hipLaunchKernelGGL((verify_kernel<D, IO, ST, 16>), dim3((unsigned)grid), dim3(64 * kWV), lds, stream, a);
+    }
   }
   return hipGetLastError();
 }
