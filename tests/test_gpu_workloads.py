@@ -6,7 +6,8 @@ heads' inputs and is compared on those heads' outputs and final states.
 Workloads (q, k ~ N(0, 1/d), v ~ N(0, 1), bf16 inputs, fp32 state):
   * prefill B=1, H=8, N=4096, d=128, block 64      -- every head checked
   * prefill B=4, H=64, N=32768, d=128, block 128   -- 6 sampled heads
-  * prefill B=1, H=64, N=1048576, d=128, block 128 -- heads 0, 21, 42, 63
+  * prefill B=1, H=64, N=1048576, d=128, block 128 -- heads 0, 21, 42, 63,
+    with the value-column split and with the sequence split
   * one of 8 segments of that sequence, B=1, H=64, N=131072: the segment's
     K^T V (state accumulation) and its prefill from a non-zero initial state
     -- heads 0, 45
@@ -35,7 +36,9 @@ def _heads_to_host(t, heads):
     return np.stack([t[b, h].to(torch.float32).cpu().numpy() for b, h in heads])
 
 
-def _check_sampled_prefill(B, H, N, d, block, cfg, heads, label):
+def _check_sampled_prefill(B, H, N, d, block, cfg, heads, label, seqsplit=False):
+    """The prefill on the whole workload, sampled heads against the oracle;
+    with seqsplit, also lin_attn_prefill_seqsplit on the same inputs."""
     t0 = time.time()
     q, k, v = synth.prefill_inputs_device(cfg, B, H, N, d)
     o = torch.empty_like(q)
@@ -44,16 +47,24 @@ def _check_sampled_prefill(B, H, N, d, block, cfg, heads, label):
     announce(label, f"inputs ready in {time.time() - t0:.1f}s")
     la.prefill(q, k, v, o, S, block)
     torch.cuda.synchronize()
+    outs = {"prefill": (np.stack([host(o[b, h]) for b, h in heads]), np.stack([host(S[b, h]) for b, h in heads]))}
+    if seqsplit:
+        assert la.prefill_seqsplit_workspace(B, H, N, d, block, torch.bfloat16) > 0
+        S.zero_()
+        la.prefill_seqsplit(q, k, v, o, S, block)
+        torch.cuda.synchronize()
+        outs["seqsplit"] = (np.stack([host(o[b, h]) for b, h in heads]),
+                            np.stack([host(S[b, h]) for b, h in heads]))
     qh, kh, vh = (_heads_to_host(t, heads) for t in (q, k, v))
-    oh = np.stack([host(o[b, h]) for b, h in heads])
-    Sh = np.stack([host(S[b, h]) for b, h in heads])
     del q, k, v, o
     torch.cuda.empty_cache()
     t1 = time.time()
     o_ref, S_ref = oracle.recurrence(qh, kh, vh)
-    eo, es = rel_err(oh, o_ref), rel_err(Sh, S_ref)
-    print(f"  {label}: heads {heads} rel err o={eo:.3e} state={es:.3e} (oracle {time.time() - t1:.1f}s)", flush=True)
-    assert eo <= TOL_BF16 and es <= TOL_BF16
+    for name, (oh, Sh) in outs.items():
+        eo, es = rel_err(oh, o_ref), rel_err(Sh, S_ref)
+        print(f"  {label} {name}: heads {heads} rel err o={eo:.3e} state={es:.3e} (oracle {time.time() - t1:.1f}s)",
+              flush=True)
+        assert eo <= TOL_BF16 and es <= TOL_BF16, name
 
 
 def test_workload_prefill_8x4096_all_heads():
@@ -88,7 +99,8 @@ def test_workload_prefill_4x64x32k_sampled():
 
 def test_workload_prefill_1m_tokens_sampled():
     announce("workload prefill B1 H64 N1048576 d128 blk128 (heads 0,21,42,63)")
-    _check_sampled_prefill(1, 64, 1 << 20, 128, 128, 4, [(0, 0), (0, 21), (0, 42), (0, 63)], "B1 H64 N1M")
+    _check_sampled_prefill(1, 64, 1 << 20, 128, 128, 4, [(0, 0), (0, 21), (0, 42), (0, 63)], "B1 H64 N1M",
+                           seqsplit=True)
 
 
 def test_workload_sequence_shard_sampled():
