@@ -36,7 +36,20 @@ struct PrefillArgs {
   const float *g_in;
   float *g_out;
   int g_in_t;
+  // second pass of a paired gradient launch (prefill_bf16_grad_pair_launch):
+  // its q, k, v, o and states, as above
+  const unsigned short *q2, *k2, *v2;
+  unsigned short *o2;
+  const float *g_in2;
+  float *g_out2;
+  int g_in_t2;
 };
+// Two reversed gradient passes of the same BH sequences in one launch: pass
+// 1 from the q, k, v, o, g_* pointers, pass 2 from the *2 pointers.  The
+// two passes must read the same key and value tensors (k2, v2 = v, k); the
+// two workgroups of a sequence then run on one XCD and share their tiles
+// through its L2.  d = 128 or 64, value columns not split.
+hipError_t prefill_bf16_grad_pair_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
 int prefill_bf16_max_block(int d);
 int prefill_bf16_max_split(int d);
 hipError_t prefill_bf16_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);

@@ -170,7 +170,21 @@ int lin_attn_backward(const void *q, const void *k, const void *v, const void *d
   // tokens it only copies dS_N, or zeros, into dS_0)
   a.q = (u16p)k; a.k = (u16p)q; a.v = (u16p)dout; a.o = (unsigned short *)dv;
   a.g_in = dstate; a.g_in_t = 0; a.g_out = dstate0;
-  hipError_t e = lal::prefill_bf16_grad_launch(a, BH, (int)d, true, s);
+  hipError_t e;
+  if (nsplit == 1 && N > 0) {
+    // dV and dK in one launch: dK is the reversed prefill of (V, dout, Q) from
+    // dS_N^T, whose keys and values are dV's values and keys, so the two
+    // workgroups of a sequence stream the same Q and dout tiles
+    a.q2 = (u16p)v; a.k2 = (u16p)dout; a.v2 = (u16p)q; a.o2 = (unsigned short *)dk;
+    a.g_in2 = dstate; a.g_in_t2 = 1; a.g_out2 = nullptr;
+    e = lal::prefill_bf16_grad_pair_launch(a, BH, (int)d, s);
+    if (e != hipSuccess) return from_hip(e);
+    // dQ: forward prefill of (dout, V, K) from S_0^T; its final state is not needed
+    a.q = (u16p)dout; a.k = (u16p)v; a.v = (u16p)k; a.o = (unsigned short *)dq;
+    a.g_in = state0; a.g_in_t = 1; a.g_out = nullptr;
+    return from_hip(lal::prefill_bf16_grad_launch(a, BH, (int)d, false, s));
+  }
+  e = lal::prefill_bf16_grad_launch(a, BH, (int)d, true, s);
   if (e != hipSuccess || N == 0) return from_hip(e);
   // dQ: forward prefill of (dout, V, K) from S_0^T; its final state is not needed
   a.q = (u16p)dout; a.k = (u16p)v; a.v = (u16p)k; a.o = (unsigned short *)dq;

@@ -80,7 +80,13 @@ enum PrefillStateMode {
   kPsBF16 = 2,     // bf16 codes of state / scale
   kPsE4M3 = 3,     // OCP FP8 E4M3 codes of state / scale
   kPsGrad = 4,     // fp32 state from g_in (optionally transposed, null = 0) to g_out (null: none)
-  kPsGradRev = 5   // as kPsGrad, with the token order reversed (suffix sums instead of prefix sums)
+  kPsGradRev = 5,  // as kPsGrad, with the token order reversed (suffix sums instead of prefix sums)
+  // as kPsGradRev, two passes in one launch: the workgroups of a sequence's
+  // two passes (value slice 0 and 1 of the nsplit = 2 mapping, the second
+  // with the *2 pointers) share an XCD and stream the same K and V tiles,
+  // which they load with the default cache policy so that L2 can serve the
+  // second reader
+  kPsGradRevPair = 6
 };
 
 // Round x / scale to the storage format of SM and return the stored value
@@ -161,6 +167,11 @@ __device__ __forceinline__ u32x4 raw_desc(const void *base, uint32_t bytes) {
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma_b128(u32x4 desc, int voff, unsigned lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
+}
+// the same with the default cache policy (tiles that a second workgroup reads)
+__device__ __forceinline__ void dma_b128_shared(u32x4 desc, int voff, unsigned lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -302,14 +313,17 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     bh = wg / nsplit;
     split = (int)(wg % nsplit);
   }
-  const int j0 = split * DV;
+  // paired gradient passes: the slice index selects the pass, not columns
+  constexpr bool PAIR_PASS = SM == kPsGradRevPair;
+  const bool second = PAIR_PASS && split == 1;
+  const int j0 = PAIR_PASS ? 0 : split * DV;
   const int64_t N = a.N;
   const int blk = a.blk;
   // Block bookkeeping in 32-bit scalars (the host guarantees N / blk < 2^31).
   const int nfull = (int)(N / blk);                       // blocks of blk tokens
   const int last = (int)(N - (int64_t)nfull * blk);       // tokens in a final partial block
   const int nblk = nfull + (last > 0 ? 1 : 0);
-  constexpr bool REV = SM == kPsGradRev;
+  constexpr bool REV = SM == kPsGradRev || SM == kPsGradRevPair;
   // first token (memory order) of the block processed at step j, of length len
   auto blk_tok0 = [&](int j, int len) -> int64_t {
     if constexpr (REV)
@@ -320,10 +334,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // state snapshots per sequence
   const int nsnap = (SM == kPsF32Snap && a.snap) ? nfull / a.snap_every : 0;
 
-  const u16 *qh = a.q + (size_t)bh * (size_t)N * D;
-  const u16 *kh = a.k + (size_t)bh * (size_t)N * D;
-  const u16 *vh = a.v + (size_t)bh * (size_t)N * D;  // slice offset j0 added per load
-  u16 *oh = a.o + (size_t)bh * (size_t)N * D + j0;
+  const u16 *qh = (second ? a.q2 : a.q) + (size_t)bh * (size_t)N * D;
+  const u16 *kh = (second ? a.k2 : a.k) + (size_t)bh * (size_t)N * D;
+  const u16 *vh = (second ? a.v2 : a.v) + (size_t)bh * (size_t)N * D;  // slice offset j0 added per load
+  u16 *oh = (second ? a.o2 : a.o) + (size_t)bh * (size_t)N * D + j0;
+  const float *g_in = second ? a.g_in2 : a.g_in;
+  const int g_in_t = second ? a.g_in_t2 : a.g_in_t;
+  float *g_out = second ? a.g_out2 : a.g_out;
   const size_t st0 = (size_t)bh * D * D + j0;  // this slice of the state (elements)
 
   constexpr int RB = D * 2;    // bytes per K row and per state-copy row
@@ -354,11 +371,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         else if constexpr (SM == kPsE4M3)
           S_acc[x][y][e] = __builtin_amdgcn_cvt_f32_fp8((int)((const uint8_t *)a.lp_state)[s_at(x, y, e)], 0) * lp_sc;
         else if constexpr (SM >= kPsGrad)
-          S_acc[x][y][e] = !a.g_in ? 0.f
-                           : a.g_in_t ? a.g_in[(size_t)bh * D * D +
-                                               (size_t)(j0 + (jb * P::BJT + y) * 16 + lr) * D +
-                                               (ib * P::BIT + x) * 16 + 4 * g + e]
-                                      : a.g_in[s_at(x, y, e)];
+          S_acc[x][y][e] = !g_in ? 0.f
+                           : g_in_t ? g_in[(size_t)bh * D * D +
+                                           (size_t)(j0 + (jb * P::BJT + y) * 16 + lr) * D +
+                                           (ib * P::BIT + x) * 16 + 4 * g + e]
+                                    : g_in[s_at(x, y, e)];
         else
           S_acc[x][y][e] = a.state[s_at(x, y, e)];
       }
@@ -505,13 +522,19 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const int row = inst * P::KRPI + lane / P::CPRK;
       const int c = swz<P::CPRK>(row, lane % P::CPRK);
       const u32x4 desc = raw_desc(kh + (size_t)d.tok0 * D, inst < P::KINST ? (uint32_t)d.len * D * 2 + zero : 0u);
-      dma_b128(desc, ((REV ? d.len - 1 - row : row) * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
+      if constexpr (PAIR_PASS)
+        dma_b128_shared(desc, ((REV ? d.len - 1 - row : row) * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
+      else
+        dma_b128(desc, ((REV ? d.len - 1 - row : row) * D + c * 8) * 2, lds_addr(d.Kd + inst * 512));
     } else {
       const int inst = wave + kWaves * (m - P::KI_W);
       const int row = inst * P::VRPI + lane / P::CPRV;
       const int c = swz<P::CPRV>(row, lane % P::CPRV);
       const u32x4 desc = raw_desc(vh + (size_t)d.tok0 * D, inst < P::VINST ? (uint32_t)d.len * D * 2 + zero : 0u);
-      dma_b128(desc, ((REV ? d.len - 1 - row : row) * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
+      if constexpr (PAIR_PASS)
+        dma_b128_shared(desc, ((REV ? d.len - 1 - row : row) * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
+      else
+        dma_b128(desc, ((REV ? d.len - 1 - row : row) * D + j0 + c * 8) * 2, lds_addr(d.Vd + inst * 512));
     }
   };
   auto kv_issue_all = [&](const KvDma &d) __attribute__((always_inline)) {
@@ -903,7 +926,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           if constexpr (SM == kPsBF16)
             ((u16 *)a.lp_state)[s_at(x, y, e)] = f32_to_bf16_bits(S_acc[x][y][e] * lp_inv);
           else if constexpr (SM >= kPsGrad) {
-            if (a.g_out) a.g_out[s_at(x, y, e)] = S_acc[x][y][e];
+            if (g_out) g_out[s_at(x, y, e)] = S_acc[x][y][e];
           } else
             a.state[s_at(x, y, e)] = S_acc[x][y][e];
         }
