@@ -91,9 +91,11 @@ def backward_bytes(B, H, N, d, **_):
 
 
 def backward_design_bytes(B, H, N, d, **_):
-    """Bytes the three passes move: each reads three bf16 inputs and writes
-    one bf16 output (24 d per token-head), plus the fp32 gradient of S_0."""
-    return B * H * (N * 24 * d + 4 * d * d)
+    """Bytes the two launches move when the dV and dK passes run paired: the
+    dQ pass reads dO, V, K and writes dq (8 d per token-head); the paired
+    launch reads K, V, Q, dO once from HBM (its second reads of Q and dO are
+    served by L2) and writes dk and dv (12 d); plus the fp32 gradient of S_0."""
+    return B * H * (N * 20 * d + 4 * d * d)
 
 
 def state_accumulate_bytes(B, H, N, d, **_):
@@ -489,7 +491,7 @@ def main():
             "hbm_GBps_design_bytes": backward_design_bytes(**P) / (avg["backward"] / 1e3) / 1e9,
             "pct_hbm_peak_design_bytes": 100 * backward_design_bytes(**P) / (avg["backward"] / 1e3) / 1e9
             / PEAK_HBM_GBS,
-            "launches": 3,
+            "launches": 2,
         },
         "decode": {
             "fp32_state_ms": avg["decode_fp32"], "fp32_state_GBps": d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9,
