@@ -350,6 +350,10 @@ def main():
         sS = torch.zeros((S["B"], S["H"], S["d"], S["d"]), dtype=torch.float32, device=dev)
         so2 = torch.empty_like(sq)
         sS2 = torch.zeros_like(sS)
+        so3 = torch.empty_like(sq)
+        sS3 = torch.zeros_like(sS)
+        sws = torch.empty(max(16, la.prefill_seqsplit_workspace(S["B"], S["H"], S["N"], S["d"], S["block"],
+                                                                torch.bfloat16)), dtype=torch.uint8, device=dev)
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     if need["shard"]:
         hq, hk, hv = synth.prefill_inputs_device(4, SH["B"], SH["H"], SH["N"], SH["d"])
@@ -376,6 +380,7 @@ def main():
                              ("decode_bf16", need["decode"]), ("decode_e4m3", need["decode"]),
                              ("verify", need["decode"]),
                              ("commit", need["decode"]), ("small_chunked", need["small"]),
+                             ("small_chunked_seqsplit", need["small"]),
                              ("small_recurrent", need["small"]), ("shard_state_accumulate", need["shard"]),
                              ("shard_state_accumulate_tiles", need["shard"]),
                              ("shard_prefill_seqsplit", need["shard"]),
@@ -404,6 +409,8 @@ def main():
             timed("small_chunked", lambda: la.prefill(sq, sk, sv, so, sS, S["block"]))
             flush.fill_(1)
             timed("small_recurrent", lambda: la.prefill_recurrent(sq, sk, sv, so2, sS2))
+            flush.fill_(0)
+            timed("small_chunked_seqsplit", lambda: la.prefill_seqsplit(sq, sk, sv, so3, sS3, S["block"], sws))
         if need["shard"]:
             timed("shard_state_accumulate", lambda: la.state_accumulate_split(hk, hv, hdS, hws))
             timed("shard_state_accumulate_tiles", lambda: la.state_accumulate(hk, hv, hdS2))
@@ -513,6 +520,8 @@ def main():
         },
         "crossover": {
             "chunked_ms": avg["small_chunked"], "recurrent_ms": avg["small_recurrent"],
+            "chunked_seqsplit_ms": avg["small_chunked_seqsplit"],
+            "chunked_seqsplit_tokens_per_s": small_tokens / (avg["small_chunked_seqsplit"] / 1e3),
             "chunked_tokens_per_s": small_tokens / (avg["small_chunked"] / 1e3),
             "recurrent_tokens_per_s": small_tokens / (avg["small_recurrent"] / 1e3),
             "cache": "each run follows a 512 MiB write that evicts the 256 MB last-level cache",
@@ -572,7 +581,9 @@ def crossover_sweep(la, synth, torch, steps: int = 20):
     (winzheng.jp), section "計算とメモリのボトルネックの不整合": a
     break-even of a few thousand tokens)?  Each launch follows a 512 MiB
     write that evicts the last-level cache; times are HIP-event averages
-    over `steps` launches.  A modeled line gives causal softmax attention at
+    over `steps` launches.  The chunked form runs as lin_attn_prefill and as
+    lin_attn_prefill_seqsplit (which cuts the sequences into parts of at
+    least 512 tokens to fill the GPU).  A modeled line gives causal softmax attention at
     the bf16 matrix peak, 2 N^2 d flop per head (not built; context only).
     """
     B, d, blk = CROSSOVER["B"], CROSSOVER["d"], CROSSOVER["block"]
@@ -585,7 +596,10 @@ def crossover_sweep(la, synth, torch, steps: int = 20):
         o = torch.empty_like(q)
         S = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
         res = {}
+        ws = torch.empty(max(16, la.prefill_seqsplit_workspace(B, H, N, d, blk, torch.bfloat16)),
+                         dtype=torch.uint8, device=dev)
         for name, fn in (("chunked", lambda: la.prefill(q, k, v, o, S, blk)),
+                         ("chunked_seqsplit", lambda: la.prefill_seqsplit(q, k, v, o, S, blk, ws)),
                          ("recurrent", lambda: la.prefill_recurrent(q, k, v, o, S))):
             ms = []
             for i in range(steps + 2):
@@ -600,11 +614,13 @@ def crossover_sweep(la, synth, torch, steps: int = 20):
             res[name] = sum(ms) / len(ms)
         softmax_ms = 2.0 * N * N * d * B * H / (PEAK_BF16_TFLOPS * 1e12) * 1e3
         rows.append({"H": H, "N": N, "chunked_ms": res["chunked"], "recurrent_ms": res["recurrent"],
+                     "chunked_seqsplit_ms": res["chunked_seqsplit"],
                      "recurrent_over_chunked": res["recurrent"] / res["chunked"],
                      "chunked_tokens_per_s": B * N / (res["chunked"] / 1e3),
                      "recurrent_tokens_per_s": B * N / (res["recurrent"] / 1e3),
                      "modeled_softmax_at_bf16_peak_ms": softmax_ms})
-        print(f"[crossover] H={H} N={N}: chunked {res['chunked']:.4f} ms, recurrent {res['recurrent']:.4f} ms",
+        print(f"[crossover] H={H} N={N}: chunked {res['chunked']:.4f} ms, seqsplit {res['chunked_seqsplit']:.4f} ms, "
+              f"recurrent {res['recurrent']:.4f} ms",
               file=sys.stderr, flush=True)
     return {"metric": "chunked vs token-by-token prefill time over N (ms per launch)",
             "config": {"workload": f"B={B} H in {list(CROSSOVER['Hs'])} d={d} block {blk}, "

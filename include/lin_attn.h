@@ -326,8 +326,9 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state,
  * Prefill cut along the tokens, for few sequences: the same outputs and
  * final state as lin_attn_prefill (up to fp32 rounding of the carried
  * state), computed as follows.  Each sequence's N tokens are cut into P equal
- * parts so that B*H*P is about 256 (one chunked-prefill workgroup per compute
- * unit; parts of at least 2048 tokens, P a power of two dividing N).  The
+ * parts so that B*H*P is at most 256 (one chunked-prefill workgroup per compute
+ * unit, before any value-column split; parts of at least 512 tokens, P a power
+ * of two dividing N).  The
  * K^T V of the first P-1 parts is summed by the token-split accumulation
  * (into the workspace); each part's initial state is S_0 plus the sums of the
  * parts before it, added in part order (the associativity equation of

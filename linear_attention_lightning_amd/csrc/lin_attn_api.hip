@@ -381,8 +381,8 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state, 
 
 namespace {
 
-// Prefill cut along the tokens: P parts per sequence (B*H*P about 256, parts of
-// at least 2048 tokens, P a power of two dividing N); the K^T V of the first
+// Prefill cut along the tokens: P parts per sequence (B*H*P at most 256, parts
+// of at least 512 tokens, P a power of two dividing N); the K^T V of the first
 // P-1 parts is summed in chunks of L/S tokens (S a power of two <= 4 dividing
 // L, chunks of at least 1024 tokens).  Workspace: (P-1) S BH partial states,
 // then BH P part states.
@@ -405,7 +405,7 @@ int seqsplit_check(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, li
   pl->S = 1;
   pl->ws_bytes = 0;
   if (io_dtype == LIN_ATTN_BF16 && BH > 0 && N > 0) {
-    while (BH * pl->P * 2 <= 256 && N % (pl->P * 2) == 0 && N / (pl->P * 2) >= 2048) pl->P *= 2;
+    while (BH * pl->P * 2 <= 256 && N % (pl->P * 2) == 0 && N / (pl->P * 2) >= 512) pl->P *= 2;
   }
   pl->L = pl->P > 0 ? N / pl->P : N;
   if (pl->P > 1) {

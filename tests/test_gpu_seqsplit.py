@@ -34,10 +34,12 @@ def gpu_seqsplit(q, k, v, S0, block, dtype="bf16", workspace=None):
 
 
 @pytest.mark.parametrize("B,H,N,d,block", [
-    (1, 4, 16384, 128, 128),   # 8 parts of 2048, 2 accumulation chunks per part
-    (2, 2, 8192, 64, 64),      # 4 parts
-    (1, 1, 4176, 128, 128),    # 2 parts of 2088: ragged last block in every part
-    (1, 3, 12288, 128, 64),
+    (1, 4, 16384, 128, 128),   # 32 parts of 512
+    (2, 2, 8192, 64, 64),      # 16 parts
+    (1, 1, 4176, 128, 128),    # 8 parts of 522: ragged last block in every part
+    (1, 3, 12288, 128, 64),    # 16 parts of 768
+    (1, 1, 65536, 128, 128),   # 64 parts of 1024, 1 accumulation chunk each
+    (1, 2, 16384, 64, 128),    # 32 parts of 512 (d = 64)
 ])
 def test_seqsplit_random(B, H, N, d, block):
     ws = la.prefill_seqsplit_workspace(B, H, N, d, block, torch.bfloat16)
@@ -76,12 +78,12 @@ def test_seqsplit_uncut_cases_and_workspace():
     the plain prefill, bitwise; a workspace one byte short is rejected; a
     cut call is bitwise repeatable."""
     announce("prefill seqsplit uncut / workspace / determinism")
-    q, k, v = synth.prefill_inputs(42, 2, 2, 3000, 128)  # 3000 tokens: no cut
+    q, k, v = synth.prefill_inputs(42, 2, 2, 1000, 128)  # 1000 tokens: no cut (parts of 500 < 512)
     S0 = random_state(3, (2, 2), 128)
-    assert la.prefill_seqsplit_workspace(2, 2, 3000, 128, 128, torch.bfloat16) == 0
+    assert la.prefill_seqsplit_workspace(2, 2, 1000, 128, 128, torch.bfloat16) == 0
     o, S = gpu_seqsplit(q, k, v, S0, 128)
     o1, S1 = gpu_prefill(q, k, v, S0, 128, "bf16")
-    np.testing.assert_array_equal(o, o1)
+    np.testing.assert_array_equal(o, o1)  # no cut: the plain prefill, bitwise
     np.testing.assert_array_equal(S, S1)
     assert la.prefill_seqsplit_workspace(4, 64, 32768, 128, 128, torch.bfloat16) == 0  # 256 sequences
     assert la.prefill_seqsplit_workspace(1, 2, 8192, 128, 64, torch.float32) == 0
