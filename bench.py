@@ -24,6 +24,9 @@ N = 256 ... 32768 at the crossover shape (see crossover_sweep).
 ``--only long`` times the long-context prefill (B=1, H=64, N=1048576, d=128,
 block 128; 16 GiB per tensor) with the value-column split and with the
 sequence split (see long_context).
+``--only decode128`` times the decode workload's 128 consecutive steps,
+launched one by one and replayed from a HIP graph (see decode_steps; the
+default run includes it).
 ``--only ceiling`` measures the HBM bandwidth a plain streaming kernel
 reaches for the path's read:write byte mixes (see hbm_ceiling); the default
 run includes it.
@@ -164,6 +167,72 @@ def cpu_baseline(heads: int = 64, min_seconds: float = 10.0, max_passes: int = 6
 
 
 LONG = dict(B=1, H=64, N=1 << 20, d=128, block=128)
+DECODE_STEPS = 128  # consecutive single-token steps of the decode workload
+
+
+def decode_steps(la, synth, torch, reps: int = 5):
+    """The decode workload's 128 consecutive single-token steps (256 x 64
+    sequences, d = 128, fp32 state from the 2048-outer-product S_0, fresh bf16
+    q, k, v each step), timed as a whole: launched one by one, and captured
+    once in a HIP graph and replayed.  The state is reset from S_0 outside
+    the timed regions.  Every replay's outputs and final state are compared
+    bitwise with the launched-one-by-one run (eager work and a
+    synchronisation between replays)."""
+    D = DECODE
+    dev = torch.device("cuda:0")
+    S0 = synth.decode_initial_state_device(D["B"], D["H"], D["d"])
+    qs, ks, vs = (torch.stack(t) for t in zip(*(synth.decode_step_inputs_device(t, D["B"], D["H"], D["d"])
+                                                  for t in range(DECODE_STEPS))))
+    S = S0.clone()
+    o = torch.empty_like(qs)
+
+    def run():
+        for t in range(DECODE_STEPS):
+            la.decode(qs[t], ks[t], vs[t], o[t], S)
+
+    def timed(fn):
+        ms = []
+        for _ in range(reps):
+            S.copy_(S0)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return sum(ms) / len(ms)
+
+    eager_ms = timed(run)
+    S_ref, o_ref = S.clone(), o.clone()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    S.copy_(S0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        run()
+    torch.cuda.synchronize()
+    same = True
+    for _ in range(3):
+        S.copy_(S0)
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = same and torch.equal(S, S_ref) and torch.equal(o, o_ref)
+        # eager work between replays
+        S.copy_(S0)
+        run()
+        torch.cuda.synchronize()
+        same = same and torch.equal(S, S_ref)
+    graph_ms = timed(graph.replay)
+    step_bytes = decode_bytes(D["B"], D["H"], D["d"], 4)
+    return {"steps": DECODE_STEPS,
+            "eager_ms": eager_ms, "eager_ms_per_step": eager_ms / DECODE_STEPS,
+            "graph_ms": graph_ms, "graph_ms_per_step": graph_ms / DECODE_STEPS,
+            "graph_GBps": step_bytes * DECODE_STEPS / (graph_ms / 1e3) / 1e9,
+            "graph_pct_hbm_peak": 100 * step_bytes * DECODE_STEPS / (graph_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "graph_replays_bitwise_equal_to_eager": bool(same)}
 
 
 def long_context(la, synth, torch, steps: int = 5):
@@ -261,7 +330,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy", "drift", "crossover",
-                                       "ceiling", "long"],
+                                       "ceiling", "long", "decode128"],
                     help="run one kernel only (for counter collection); prints timings, no JSON")
     args = ap.parse_args()
 
@@ -289,6 +358,9 @@ def main():
         print(json.dumps(crossover_sweep(la, synth, torch, steps=args.steps)))
         return
 
+    if args.only == "decode128":
+        print(json.dumps(decode_steps(la, synth, torch)))
+        return
     if args.only == "long":
         print(json.dumps(long_context(la, synth, torch)))
         return
@@ -443,6 +515,7 @@ def main():
         return
 
     ceiling = hbm_ceiling(torch)
+    steps128 = decode_steps(la, synth, torch)
     p_bytes = prefill_bytes(**P)
     p_flops = prefill_flops(**P)
     p_dense = prefill_dense_flops(**P)
@@ -510,6 +583,7 @@ def main():
             "tokens_per_s_fp32_state": D["B"] / (avg["decode_fp32"] / 1e3),
             "fp32_state_pct_of_1to1_stream_ceiling": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9
             / ceiling["r1w1_GBps"],
+            "steps_128": steps128,
             "speculative": {
                 "drafts": DRAFTS, "accepted": DRAFTS - 1,
                 "verify_ms": avg["verify"], "commit_ms": avg["commit"],
