@@ -156,10 +156,18 @@ def cpu_baseline(heads: int = 64, min_seconds: float = 10.0, max_passes: int = 6
         if dt >= min_seconds or passes >= max_passes:
             break
     head_tokens = heads * N * passes
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": head_tokens / dt / H,
         "unit": "tokens/s",
         "cores": min(threads, heads),
+        "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"{heads} of the 256 sequences (N=32768, d=128, fp64 token-by-token recurrence), "
                   f"{passes} passes in {dt:.2f} s; {head_tokens * 4 * d * d / dt / 1e9:.1f} GFLOP/s fp64",
