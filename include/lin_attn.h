@@ -367,7 +367,11 @@ int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void 
  * prefill of (dout, V, K) from S_0^T, and dV and dK are prefills of
  * (K, Q, dout) from dstate and of (V, dout, Q) from dstate^T taken over the
  * reversed token order (suffix sums); the first of those ends in dstate0.
- * They run as three launches on `stream`.
+ * dV and dK share their keys and values (q and dout, swapped) and the carried
+ * state (G and G^T): when the B*H sequences fill the GPU without splitting
+ * value columns, they run fused, one reversed sweep per sequence that stages
+ * each q and dout tile once for both (strategy LIN_ATTN_BWD_FUSED below);
+ * otherwise as separate passes.  All launches go on `stream`.
  *
  * q, k, v, dout  : [B][H][N][d] of io_dtype (read only)
  * state0         : [B][H][d][d] fp32, the S_0 of the forward call, or NULL
@@ -387,6 +391,25 @@ int lin_attn_backward(const void *q, const void *k, const void *v, const void *d
                       const float *state0, const float *dstate, void *dq, void *dk, void *dv,
                       float *dstate0, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
                       lin_attn_dtype_t io_dtype, void *stream);
+
+/*
+ * lin_attn_backward with the way the dV and dK passes run chosen by the
+ * caller (the results agree to fp32 rounding of the carried states; the
+ * separate, paired and fused forms give bitwise equal gradients):
+ *   LIN_ATTN_BWD_AUTO     as lin_attn_backward;
+ *   LIN_ATTN_BWD_SEPARATE two launches, value columns split while B*H alone
+ *                         leaves compute units idle;
+ *   LIN_ATTN_BWD_PAIRED   one launch of 2*B*H workgroups: a sequence's dV and
+ *                         dK workgroups share an XCD and read the same q and
+ *                         dout tiles, the second reader served by its L2;
+ *   LIN_ATTN_BWD_FUSED    one workgroup per sequence computes both.
+ * Any other value gives LIN_ATTN_EINVAL.  Other arguments as lin_attn_backward.
+ */
+enum { LIN_ATTN_BWD_AUTO = 0, LIN_ATTN_BWD_SEPARATE = 1, LIN_ATTN_BWD_PAIRED = 2, LIN_ATTN_BWD_FUSED = 3 };
+int lin_attn_backward_ex(const void *q, const void *k, const void *v, const void *dout,
+                         const float *state0, const float *dstate, void *dq, void *dk, void *dv,
+                         float *dstate0, int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                         lin_attn_dtype_t io_dtype, int64_t strategy, void *stream);
 
 /* Static, human-readable text for a return code (never NULL). */
 const char *lin_attn_strerror(int code);

@@ -6,6 +6,10 @@ The computation runs in hand-written HIP kernels behind the C ABI of
 input generator used by the tests and the benchmark (``synth``).
 """
 from ._binding import (  # noqa: F401
+    BWD_AUTO,
+    BWD_FUSED,
+    BWD_PAIRED,
+    BWD_SEPARATE,
     BF16,
     EHIP,
     EINVAL,
@@ -33,7 +37,7 @@ from ._binding import (  # noqa: F401
     strerror,
 )
 
-__all__ = ["prefill", "prefill_scaled", "prefill_seqsplit", "prefill_seqsplit_workspace", "backward", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
+__all__ = ["BWD_AUTO", "BWD_SEPARATE", "BWD_PAIRED", "BWD_FUSED", "prefill", "prefill_scaled", "prefill_seqsplit", "prefill_seqsplit_workspace", "backward", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
            "prefill_snapshots", "snapshot_count", "state_accumulate", "state_accumulate_split",
            "state_accumulate_split_workspace", "strerror", "library", "LinAttnError",
            "F32", "BF16", "FP8_E4M3", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]

@@ -72,6 +72,8 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_decode_commit_scaled.restype = i32
             lib.lin_attn_backward.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
             lib.lin_attn_backward.restype = i32
+            lib.lin_attn_backward_ex.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, i64, p]
+            lib.lin_attn_backward_ex.restype = i32
             lib.lin_attn_strerror.argtypes = [i32]
             lib.lin_attn_strerror.restype = ctypes.c_char_p
             _lib = lib
@@ -411,7 +413,12 @@ def decode_commit(k, v, state, accept=None, *, state_scale=None, stream=None):
     return state
 
 
-def backward(q, k, v, dout, dq, dk, dv, block: int, *, state0=None, dstate=None, dstate0=None, stream=None):
+# how the dV and dK passes run (lin_attn_backward_ex)
+BWD_AUTO, BWD_SEPARATE, BWD_PAIRED, BWD_FUSED = 0, 1, 2, 3
+
+
+def backward(q, k, v, dout, dq, dk, dv, block: int, *, state0=None, dstate=None, dstate0=None, strategy=BWD_AUTO,
+             stream=None):
     """Gradients of the chunked prefill (``lin_attn_backward``).
 
     q, k, v, dout, dq, dk, dv: [B, H, N, d] bf16 (dq, dk, dv written);
@@ -430,9 +437,9 @@ def backward(q, k, v, dout, dq, dk, dv, block: int, *, state0=None, dstate=None,
         else:
             _check(t, name, (B, H, d, d), torch.float32, q.device)
             ptrs.append(t.data_ptr())
-    rc = library().lin_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), ptrs[0], ptrs[1],
-                                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ptrs[2], B, H, N, d, int(block),
-                                     _dtype_code(q), _stream(stream, q.device))
+    rc = library().lin_attn_backward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), ptrs[0],
+                                        ptrs[1], dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ptrs[2], B, H, N, d,
+                                        int(block), _dtype_code(q), int(strategy), _stream(stream, q.device))
     if rc != OK:
-        raise LinAttnError(rc, "lin_attn_backward")
+        raise LinAttnError(rc, "lin_attn_backward_ex")
     return dq, dk, dv

@@ -50,6 +50,11 @@ struct PrefillArgs {
 // two workgroups of a sequence then run on one XCD and share their tiles
 // through its L2.  d = 128 or 64, value columns not split.
 hipError_t prefill_bf16_grad_pair_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
+// The dV and dK passes fused in one reversed sweep per sequence: q tiles
+// from k, dout tiles from v (staged once), dV role queries from q with
+// outputs to o, dK role queries from q2 with outputs to o2; G from g_in (not
+// transposed), dS_0 to g_out.  Value columns not split.
+hipError_t prefill_bf16_grad_fused_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
 int prefill_bf16_max_block(int d);
 int prefill_bf16_max_split(int d);
 hipError_t prefill_bf16_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);

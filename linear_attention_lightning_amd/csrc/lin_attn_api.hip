@@ -134,11 +134,13 @@ int lin_attn_prefill_scaled(const void *q, const void *k, const void *v, void *o
                       (int)round_carry);
 }
 
-int lin_attn_backward(const void *q, const void *k, const void *v, const void *dout, const float *state0,
-                      const float *dstate, void *dq, void *dk, void *dv, float *dstate0, int64_t B,
-                      int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
-                      void *stream) {
+namespace {
+
+int backward_impl(const void *q, const void *k, const void *v, const void *dout, const float *state0,
+                  const float *dstate, void *dq, void *dk, void *dv, float *dstate0, int64_t B, int64_t H,
+                  int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype, int64_t strategy, void *stream) {
   if (B < 0 || H < 0 || N < 0 || d < 0 || block < 0) return LIN_ATTN_EINVAL;
+  if (strategy < LIN_ATTN_BWD_AUTO || strategy > LIN_ATTN_BWD_FUSED) return LIN_ATTN_EINVAL;
   if (io_dtype != LIN_ATTN_BF16 && io_dtype != LIN_ATTN_F32) return LIN_ATTN_EUNSUPPORTED;
   if (io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;  // the bf16 matrix-core kernel only
   if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
@@ -159,42 +161,74 @@ int lin_attn_backward(const void *q, const void *k, const void *v, const void *d
   if (rc != LIN_ATTN_OK) return rc;
   int nsplit = 1;
   while (nsplit < lal::prefill_bf16_max_split((int)d) && BH * nsplit < cus) nsplit *= 2;
-  if (BH * nsplit > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  // auto: the fused dK/dV sweep when the sequences fill the GPU without a
+  // value split, else separate passes with the split
+  const int64_t strat = strategy != LIN_ATTN_BWD_AUTO ? strategy
+                        : (nsplit == 1 ? LIN_ATTN_BWD_FUSED : LIN_ATTN_BWD_SEPARATE);
+  if (strat != LIN_ATTN_BWD_SEPARATE) nsplit = 1;
+  if (BH * 2 * nsplit > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
   if (N / block > 0x7ffffff0) return LIN_ATTN_EUNSUPPORTED;
   using u16p = const unsigned short *;
   lal::PrefillArgs a{};
   a.N = N;
   a.blk = (int)block;
   a.nsplit = nsplit;
-  // dV: reversed prefill of (K, Q, dout) from dS_N; it ends in dS_0 (with no
-  // tokens it only copies dS_N, or zeros, into dS_0)
-  a.q = (u16p)k; a.k = (u16p)q; a.v = (u16p)dout; a.o = (unsigned short *)dv;
-  a.g_in = dstate; a.g_in_t = 0; a.g_out = dstate0;
   hipError_t e;
-  if (nsplit == 1 && N > 0) {
-    // dV and dK in one launch: dK is the reversed prefill of (V, dout, Q) from
-    // dS_N^T, whose keys and values are dV's values and keys, so the two
+  if (N > 0 && strat == LIN_ATTN_BWD_FUSED) {
+    // dK and dV in one reversed sweep: q and dout tiles staged once, the k
+    // rows (dV role) and v rows (dK role) as queries, G from dS_N to dS_0
+    a.q = (u16p)k; a.k = (u16p)q; a.v = (u16p)dout; a.o = (unsigned short *)dv;
+    a.q2 = (u16p)v; a.o2 = (unsigned short *)dk;
+    a.g_in = dstate; a.g_in_t = 0; a.g_out = dstate0;
+    e = lal::prefill_bf16_grad_fused_launch(a, BH, (int)d, s);
+  } else if (N > 0 && strat == LIN_ATTN_BWD_PAIRED) {
+    // dV and dK in one launch: dK is the reversed prefill of (V, dout, Q)
+    // from dS_N^T, whose keys and values are dV's values and keys, so the two
     // workgroups of a sequence stream the same Q and dout tiles
+    a.q = (u16p)k; a.k = (u16p)q; a.v = (u16p)dout; a.o = (unsigned short *)dv;
+    a.g_in = dstate; a.g_in_t = 0; a.g_out = dstate0;
     a.q2 = (u16p)v; a.k2 = (u16p)dout; a.v2 = (u16p)q; a.o2 = (unsigned short *)dk;
     a.g_in2 = dstate; a.g_in_t2 = 1; a.g_out2 = nullptr;
     e = lal::prefill_bf16_grad_pair_launch(a, BH, (int)d, s);
-    if (e != hipSuccess) return from_hip(e);
-    // dQ: forward prefill of (dout, V, K) from S_0^T; its final state is not needed
-    a.q = (u16p)dout; a.k = (u16p)v; a.v = (u16p)k; a.o = (unsigned short *)dq;
-    a.g_in = state0; a.g_in_t = 1; a.g_out = nullptr;
-    return from_hip(lal::prefill_bf16_grad_launch(a, BH, (int)d, false, s));
+  } else {
+    // dV: reversed prefill of (K, Q, dout) from dS_N; it ends in dS_0 (with no
+    // tokens it only copies dS_N, or zeros, into dS_0)
+    a.q = (u16p)k; a.k = (u16p)q; a.v = (u16p)dout; a.o = (unsigned short *)dv;
+    a.g_in = dstate; a.g_in_t = 0; a.g_out = dstate0;
+    e = lal::prefill_bf16_grad_launch(a, BH, (int)d, true, s);
+    if (e != hipSuccess || N == 0) return from_hip(e);
+    // dK: reversed prefill of (V, dout, Q) from dS_N^T
+    a.q = (u16p)v; a.k = (u16p)dout; a.v = (u16p)q; a.o = (unsigned short *)dk;
+    a.g_in = dstate; a.g_in_t = 1; a.g_out = nullptr;
+    e = lal::prefill_bf16_grad_launch(a, BH, (int)d, true, s);
   }
-  e = lal::prefill_bf16_grad_launch(a, BH, (int)d, true, s);
-  if (e != hipSuccess || N == 0) return from_hip(e);
+  if (e != hipSuccess) return from_hip(e);
   // dQ: forward prefill of (dout, V, K) from S_0^T; its final state is not needed
+  a = lal::PrefillArgs{};
+  a.N = N;
+  a.blk = (int)block;
+  a.nsplit = nsplit;
   a.q = (u16p)dout; a.k = (u16p)v; a.v = (u16p)k; a.o = (unsigned short *)dq;
   a.g_in = state0; a.g_in_t = 1; a.g_out = nullptr;
-  e = lal::prefill_bf16_grad_launch(a, BH, (int)d, false, s);
-  if (e != hipSuccess) return from_hip(e);
-  // dK: reversed prefill of (V, dout, Q) from dS_N^T
-  a.q = (u16p)v; a.k = (u16p)dout; a.v = (u16p)q; a.o = (unsigned short *)dk;
-  a.g_in = dstate; a.g_in_t = 1; a.g_out = nullptr;
-  return from_hip(lal::prefill_bf16_grad_launch(a, BH, (int)d, true, s));
+  return from_hip(lal::prefill_bf16_grad_launch(a, BH, (int)d, false, s));
+}
+
+}  // namespace
+
+int lin_attn_backward(const void *q, const void *k, const void *v, const void *dout, const float *state0,
+                      const float *dstate, void *dq, void *dk, void *dv, float *dstate0, int64_t B,
+                      int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
+                      void *stream) {
+  return backward_impl(q, k, v, dout, state0, dstate, dq, dk, dv, dstate0, B, H, N, d, block, io_dtype,
+                       LIN_ATTN_BWD_AUTO, stream);
+}
+
+int lin_attn_backward_ex(const void *q, const void *k, const void *v, const void *dout, const float *state0,
+                         const float *dstate, void *dq, void *dk, void *dv, float *dstate0, int64_t B,
+                         int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
+                         int64_t strategy, void *stream) {
+  return backward_impl(q, k, v, dout, state0, dstate, dq, dk, dv, dstate0, B, H, N, d, block, io_dtype,
+                       strategy, stream);
 }
 
 int lin_attn_prefill(const void *q, const void *k, const void *v, void *o, float *state, int64_t B,

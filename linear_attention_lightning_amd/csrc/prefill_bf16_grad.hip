@@ -20,4 +20,12 @@ hipError_t prefill_bf16_grad_pair_launch(PrefillArgs a, int64_t BH, int d, hipSt
   return hipErrorInvalidValue;
 }
 
+hipError_t prefill_bf16_grad_fused_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream) {
+  a.nsplit = 1;
+  a.xcd_map = 0;
+  if (d == 128) return launch_nt<128, 128, kPsGradFused>(a, BH, stream);
+  if (d == 64) return launch_nt<64, 64, kPsGradFused>(a, BH, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace lal

@@ -86,7 +86,12 @@ enum PrefillStateMode {
   // with the *2 pointers) share an XCD and stream the same K and V tiles,
   // which they load with the default cache policy so that L2 can serve the
   // second reader
-  kPsGradRevPair = 6
+  kPsGradRevPair = 6,
+  // the dV and dK passes fused (reversed order, value columns not split): the
+  // K and V tiles staged in LDS are those of q and dout, read once for both;
+  // the dV role takes the k rows as queries and the carried state G as is,
+  // the dK role the v rows and G transposed (q2 = v rows, o2 = dk)
+  kPsGradFused = 7
 };
 
 // Round x / scale to the storage format of SM and return the stored value
@@ -323,7 +328,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int nfull = (int)(N / blk);                       // blocks of blk tokens
   const int last = (int)(N - (int64_t)nfull * blk);       // tokens in a final partial block
   const int nblk = nfull + (last > 0 ? 1 : 0);
-  constexpr bool REV = SM == kPsGradRev || SM == kPsGradRevPair;
+  constexpr bool REV = SM == kPsGradRev || SM == kPsGradRevPair || SM == kPsGradFused;
+  constexpr bool FUSED = SM == kPsGradFused;
   // first token (memory order) of the block processed at step j, of length len
   auto blk_tok0 = [&](int j, int len) -> int64_t {
     if constexpr (REV)
@@ -338,6 +344,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const u16 *kh = (second ? a.k2 : a.k) + (size_t)bh * (size_t)N * D;
   const u16 *vh = (second ? a.v2 : a.v) + (size_t)bh * (size_t)N * D;  // slice offset j0 added per load
   u16 *oh = (second ? a.o2 : a.o) + (size_t)bh * (size_t)N * D + j0;
+  // fused dK/dV: the second role's queries (v rows) and outputs (dk)
+  const u16 *qh2 = FUSED ? a.q2 + (size_t)bh * (size_t)N * D : nullptr;
+  u16 *oh2 = FUSED ? a.o2 + (size_t)bh * (size_t)N * D : nullptr;
   const float *g_in = second ? a.g_in2 : a.g_in;
   const int g_in_t = second ? a.g_in_t2 : a.g_in_t;
   float *g_out = second ? a.g_out2 : a.g_out;
@@ -439,6 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
   // ---- Q rows of the wave's two row tiles (registers) ----
   bf16x8 bq[2][P::NKC], qn[2][P::NKC];
+  bf16x8 qv[2][P::NKC];  // fused dK/dV: the block's v rows (the dK role's queries)
   // Row tiles of the wave's pair: T0 = rg and T1 = NT-1-rg.  Waves without
   // phase-A work load and store nothing through zero-size descriptors, so
   // that every wave issues the same vector-memory operations.
@@ -449,10 +459,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // of the line.  Each row's line is read by one instruction, so the L1 sends
   // it to L2 as one 128-byte request; the operand fragments are rearranged
   // from these registers at the start of the block that uses them (take_q).
-  auto load_q_part = [&](int64_t tok0, int len, int u, int m) __attribute__((always_inline)) {
+  // (vrows: the fused kernel's v rows into qv, else the query rows into qn)
+  auto load_q_part = [&](int64_t tok0, int len, int u, int m, bool vrows = false) __attribute__((always_inline)) {
     // descriptor built from scalar-forced words: with the generic builder the
     // compiler could not prove it uniform and looped over lanes per load
-    const u32x4 dq = raw_desc(qh + (size_t)tok0 * D, act ? (uint32_t)len * D * 2 : 0u);
+    const u32x4 dq = raw_desc((vrows ? qh2 : qh) + (size_t)tok0 * D, act ? (uint32_t)len * D * 2 : 0u);
     __amdgpu_buffer_rsrc_t rq;
     __builtin_memcpy(&rq, &dq, sizeof(rq));
     const LaneOff lo = lane_off();
@@ -461,8 +472,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     if constexpr (REV) {
       // row 16 T + r is token len-1-16T-r of the span (negative: padding)
       const int qrow = len - 1 - 16 * (u ? T1 : T0) - 8 * h - (lo.lr & 7);
-      qn[u][m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rq, (qrow * D + col) * 2, l * 128, 2));
+      const bf16x8 x = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rq, (qrow * D + col) * 2, l * 128, 2));
+      if (vrows)
+        qv[u][m] = x;
+      else
+        qn[u][m] = x;
     } else {
       const int qlane = ((lo.lr & 7) * D + col) * 2;
       qn[u][m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
@@ -475,13 +490,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // other way round.  A row rotation by 8 (DPP row_ror:8) written only to the
   // lanes of the upper (bank mask 0xc) or the lower (0x3) half of each row
   // does each in one move per dword.
-  auto take_q = [&]() __attribute__((always_inline)) {
+  auto take_q = [&](bool vrows = false) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int l = 0; l < P::NKC / 2; ++l) {
-        const u32x4 a = __builtin_bit_cast(u32x4, qn[u][2 * l]);
-        const u32x4 b = __builtin_bit_cast(u32x4, qn[u][2 * l + 1]);
+        const u32x4 a = __builtin_bit_cast(u32x4, vrows ? qv[u][2 * l] : qn[u][2 * l]);
+        const u32x4 b = __builtin_bit_cast(u32x4, vrows ? qv[u][2 * l + 1] : qn[u][2 * l + 1]);
         u32x4 e, o;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -545,8 +560,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
 
   // ---- phase A for row-tile pair {RGI, NT-1-RGI}: output rows ----
-  auto phase_a = [&](auto rgi, const u16 *Kc, const u16 *Vc, f32x4 (&acc)[2][P::NJC], auto &&vm_slot)
-                     __attribute__((always_inline)) {
+  // (tstate: read the state copy transposed, for the fused kernel's dK role)
+  auto phase_a = [&](auto rgi, const u16 *Kc, const u16 *Vc, f32x4 (&acc)[2][P::NJC], auto &&vm_slot,
+                     auto tstate) __attribute__((always_inline)) {
+    constexpr bool TS = decltype(tstate)::value;
 
     constexpr int T[2] = {decltype(rgi)::value, NT - 1 - decltype(rgi)::value};
     constexpr int NCH = T[1] / 2 + 1;  // 32-key chunks this pair touches
@@ -586,7 +603,23 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     bf16x8 sfr[P::NKC][P::NJC];
     auto load_s = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
-      for (int jl = 0; jl < P::NJC; ++jl) sfr[kc][jl] = ld128(SsT, kf[kc] + (jc0 + jl) * 16 * RB);
+      for (int jl = 0; jl < P::NJC; ++jl) {
+        if constexpr (TS) {
+          // A = S itself: lane (i, g) needs S[16 (jc0 + jl) + i][8 tau + e],
+          // tau = 8 (kc / 2) + 2 g + kc % 2 (the head-dimension order of the
+          // query fragments), i.e. column 16 (jc0 + jl) + i of rows
+          // 8 tau + e of the copy: two transposing reads whose 16 lanes
+          // address rows 8 tau + lr / 4 (+ 4) and columns + 4 (lr % 4)
+          const LaneOff lt = lane_off();
+          const int tau = 8 * (kc >> 1) + 2 * lt.g + (kc & 1);
+          const int r0 = 8 * tau + (lt.lr >> 2), r1 = r0 + 4;
+          const int ch = 2 * (jc0 + jl) + lt.h;
+          sfr[kc][jl] = ldtr(SsT, r0 * RB + (swz<P::CPRK>(r0, ch) << 4) + lt.lo8,
+                             r1 * RB + (swz<P::CPRK>(r1, ch) << 4) + lt.lo8);
+        } else {
+          sfr[kc][jl] = ld128(SsT, kf[kc] + (jc0 + jl) * 16 * RB);
+        }
+      }
     };
     load_s(0);
 #pragma unroll
@@ -676,9 +709,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // ---- output rows of the wave's pair: acc[u][jl][e] =
   // O[16 T_u + lr][(jc0 + jl) * 16 + 4g + e].  Rows past len fall outside the
   // descriptor and are dropped, so every wave issues the same stores. ----
-  auto store_o_part = [&](int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jl)
+  auto store_o_part = [&](u16 *obase, int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jl)
                           __attribute__((always_inline)) {
-    const u32x4 dod = raw_desc(oh + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
+    const u32x4 dod = raw_desc(obase + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
     __amdgpu_buffer_rsrc_t ro;
     __builtin_memcpy(&ro, &dod, sizeof(ro));
     // The row-tile part of the offset goes in the scalar offset, so each
@@ -704,9 +737,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // values 8 g .. 8 g + 7 of the pair (16 bytes), so each row of the pair is
   // written as 64 contiguous bytes: half the store instructions, and half
   // the write requests, each holding an L1 slot.
-  auto store_o_pair = [&](int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jp)
+  auto store_o_pair = [&](u16 *obase, int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jp)
                           __attribute__((always_inline)) {
-    const u32x4 dod = raw_desc(oh + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
+    const u32x4 dod = raw_desc(obase + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
     __amdgpu_buffer_rsrc_t ro;
     __builtin_memcpy(&ro, &dod, sizeof(ro));
     const uint2 ta = packed[u][2 * jp], tb = packed[u][2 * jp + 1];
@@ -732,9 +765,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   // B (bytes 64..127).  Lanes lr and lr ^ 8 of a 16-lane row then trade one of
   // them (a rotation by 8 within the row): store h writes tokens 8 h .. 8 h + 7,
   // the lanes lr < 8 holding bytes 0..63 and the lanes lr >= 8 bytes 64..127.
-  auto store_o_quad = [&](int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jq)
+  auto store_o_quad = [&](u16 *obase, int64_t tok0, int len, const uint2 (&packed)[2][P::NJC], int u, int jq)
                           __attribute__((always_inline)) {
-    const u32x4 dod = raw_desc(oh + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
+    const u32x4 dod = raw_desc(obase + (size_t)tok0 * D, act ? (uint32_t)(len * D - j0) * 2 : 0u);
     __amdgpu_buffer_rsrc_t ro;
     __builtin_memcpy(&ro, &dod, sizeof(ro));
     u32x4 pr[2];
@@ -815,7 +848,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
       for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (act) {
-      with_rg([&](auto rgi) { phase_a(rgi, Kc, Vc, acc, vm_slot); });
+      with_rg([&](auto rgi) { phase_a(rgi, Kc, Vc, acc, vm_slot, std::false_type{}); });
     } else {
 #pragma unroll
       for (int slot = 0; slot < P::NSLOT; ++slot) vm_slot(slot);
@@ -841,11 +874,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
       for (int i = cc * P::NSTI / P::NCC; i < (cc + 1) * P::NSTI / P::NCC; ++i) {
         if constexpr (P::QUAD)
-          store_o_quad(tok0, len, packed, i / (P::NJC / 4), i % (P::NJC / 4));
+          store_o_quad(oh, tok0, len, packed, i / (P::NJC / 4), i % (P::NJC / 4));
         else if constexpr (P::PAIR)
-          store_o_pair(tok0, len, packed, i / (P::NJC / 2), i % (P::NJC / 2));
+          store_o_pair(oh, tok0, len, packed, i / (P::NJC / 2), i % (P::NJC / 2));
         else
-          store_o_part(tok0, len, packed, i / P::NJC, i % P::NJC);
+          store_o_part(oh, tok0, len, packed, i / P::NJC, i % P::NJC);
       }
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 ka[P::BIT], vb[P::BJT];
@@ -887,10 +920,144 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     write_state_copy();  // bf16 copy of S_jblk for the next block's phase A
   };
 
+  // ---- one block of the fused dK/dV kernel (reversed order).  The stages
+  // hold the block's q tile (Kc) and dout tile (Vc).  On entry the block's
+  // tiles and k rows, then the previous block's dk stores, may be in flight.
+  //  1. dV role: queries = k rows, keys = q, values = dout, state G as is;
+  //  2. dK role: queries = v rows, keys = dout, values = q, state G^T;
+  //  3. G += q^T dout.
+  // The next block's k rows are issued at the start and its v rows between the
+  // roles, in common code (each set is consumed one block later, so the
+  // compiler's waits for them find every later load already counted); the
+  // next block's tiles over both roles' issue slots, the dv stores over the
+  // dK role's and the dk stores over step 3: memory work in every phase.
+  auto body_fused = [&](int jblk, const u16 *Kc, const u16 *Vc, u16 *Kn, u16 *Vn) __attribute__((always_inline)) {
+    const int64_t tok0 = blk_tok0(jblk, block_len(jblk));
+    const int len = block_len(jblk);
+    const int nlen = jblk + 1 < nblk ? block_len(jblk + 1) : 0;
+    const int64_t ntok0 = blk_tok0(jblk + 1, nlen);
+    wait_vmcnt(jblk == 0 ? 0 : P::NST);
+    take_q();
+    lds_barrier();
+    const KvDma dma = kv_prepare(ntok0, nlen, Kn, Vn);
+#pragma unroll
+    for (int kc = 0; kc < P::NKC; ++kc) {
+      load_q_part(ntok0, nlen, 0, kc);
+      load_q_part(ntok0, nlen, 1, kc);
+    }
+
+    // 1. dV role, with the next block's tiles
+    f32x4 acc[2][P::NJC];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the first half of the next block's direct loads over the dV role's
+    // issue slots, the second half over the dK role's (reads in flight
+    // through both roles)
+    constexpr int NDH = P::N_DMA / 2;
+    auto dma_slot = [&](int slot) __attribute__((always_inline)) {
+      if (nlen > 0) {
+#pragma unroll
+        for (int m = slot * NDH / P::NSLOT; m < (slot + 1) * NDH / P::NSLOT; ++m) kv_issue(dma, m);
+      }
+    };
+    if (act) {
+      with_rg([&](auto rgi) { phase_a(rgi, Kc, Vc, acc, dma_slot, std::false_type{}); });
+    } else {
+#pragma unroll
+      for (int slot = 0; slot < P::NSLOT; ++slot) dma_slot(slot);
+    }
+    uint2 packed_v[2][P::NJC];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) packed_v[u][jl] = pack_bf16x4(acc[u][jl]);
+
+    // 2. dK role, with this block's dv stores; the next block's v rows first
+    take_q(true);
+#pragma unroll
+    for (int kc = 0; kc < P::NKC; ++kc) {
+      load_q_part(ntok0, nlen, 0, kc, true);
+      load_q_part(ntok0, nlen, 1, kc, true);
+    }
+    auto vm_slot = [&](int slot) __attribute__((always_inline)) {
+      if (nlen > 0) {
+#pragma unroll
+        for (int m = NDH + slot * (P::N_DMA - NDH) / P::NSLOT; m < NDH + (slot + 1) * (P::N_DMA - NDH) / P::NSLOT; ++m)
+          kv_issue(dma, m);
+      }
+#pragma unroll
+      for (int i = slot * P::NSTI / P::NSLOT; i < (slot + 1) * P::NSTI / P::NSLOT; ++i) {
+        if constexpr (P::QUAD)
+          store_o_quad(oh, tok0, len, packed_v, i / (P::NJC / 4), i % (P::NJC / 4));
+        else if constexpr (P::PAIR)
+          store_o_pair(oh, tok0, len, packed_v, i / (P::NJC / 2), i % (P::NJC / 2));
+        else
+          store_o_part(oh, tok0, len, packed_v, i / P::NJC, i % P::NJC);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) acc[u][jl] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (act) {
+      with_rg([&](auto rgi) { phase_a(rgi, Vc, Kc, acc, vm_slot, std::true_type{}); });
+    } else {
+#pragma unroll
+      for (int slot = 0; slot < P::NSLOT; ++slot) vm_slot(slot);
+    }
+    uint2 packed_k[2][P::NJC];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int jl = 0; jl < P::NJC; ++jl) packed_k[u][jl] = pack_bf16x4(acc[u][jl]);
+
+    // 3. G += q^T dout, with this block's dk stores
+    const LaneOff lob = lane_off();
+    int ktrB[P::BIT], vtrB[P::BJT];
+#pragma unroll
+    for (int x = 0; x < P::BIT; ++x) ktrB[x] = ktr(lob, ib * P::BIT + x);
+#pragma unroll
+    for (int y = 0; y < P::BJT; ++y) vtrB[y] = vtr(lob, jb * P::BJT + y);
+#pragma unroll
+    for (int cc = 0; cc < P::NCC; ++cc) {
+      const int c0 = 32 * cc;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = cc * P::NSTI / P::NCC; i < (cc + 1) * P::NSTI / P::NCC; ++i) {
+        if constexpr (P::QUAD)
+          store_o_quad(oh2, tok0, len, packed_k, i / (P::NJC / 4), i % (P::NJC / 4));
+        else if constexpr (P::PAIR)
+          store_o_pair(oh2, tok0, len, packed_k, i / (P::NJC / 2), i % (P::NJC / 2));
+        else
+          store_o_part(oh2, tok0, len, packed_k, i / P::NJC, i % P::NJC);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 ka[P::BIT], vb[P::BJT];
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x) ka[x] = ldtr(Kc, ktrB[x] + c0 * RB, ktrB[x] + (c0 + 16) * RB);
+#pragma unroll
+      for (int y = 0; y < P::BJT; ++y) vb[y] = ldtr(Vc, vtrB[y] + c0 * VRB, vtrB[y] + (c0 + 16) * VRB);
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y) S_acc[x][y] = mfma_16x16x32(ka[x], vb[y], S_acc[x][y]);
+    }
+    lds_barrier();
+    write_state_copy();
+  };
+
   {
     const int len0 = block_len(0);
     kv_issue_all(kv_prepare(REV ? blk_tok0(0, len0) : 0, len0, Ks0, Vs0));
     load_q(REV ? blk_tok0(0, len0) : 0, len0);
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kc = 0; kc < P::NKC; ++kc) load_q_part(blk_tok0(0, len0), len0, u, kc, true);
+    }
     // The initial state and the first Q rows are consumed here, before the
     // loop, so the compiler's waits for their loads stay out of the
     // pipelined loop (where they would drain the loads in flight).
@@ -899,10 +1066,21 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int kc = 0; kc < P::NKC; ++kc) asm volatile("" ::"v"(qn[u][kc]));
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kc = 0; kc < P::NKC; ++kc) asm volatile("" ::"v"(qv[u][kc]));
+    }
   }
   for (int jblk = 0; jblk < nblk; jblk += 2) {
-    body(jblk, Ks0, Vs0, Ks1, Vs1);
-    if (jblk + 1 < nblk) body(jblk + 1, Ks1, Vs1, Ks0, Vs0);
+    if constexpr (FUSED) {
+      body_fused(jblk, Ks0, Vs0, Ks1, Vs1);
+      if (jblk + 1 < nblk) body_fused(jblk + 1, Ks1, Vs1, Ks0, Vs0);
+    } else {
+      body(jblk, Ks0, Vs0, Ks1, Vs1);
+      if (jblk + 1 < nblk) body(jblk + 1, Ks1, Vs1, Ks0, Vs0);
+    }
   }
 
   // ---- final state ----

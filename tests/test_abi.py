@@ -337,3 +337,15 @@ def test_seqsplit_workspace_query_and_validation():
     assert f(*args, FAKE, need - 1, None) == la.EINVAL
     assert f(*args, None, need, None) == la.EINVAL
     assert f(FAKE, FAKE, FAKE, MISALIGNED, FAKE, 1, 8, 8192, 128, 128, la.BF16, FAKE, need, None) == la.EINVAL
+
+
+def test_backward_strategy_validation():
+    lib = la.library()
+    f = lib.lin_attn_backward_ex
+    args = (FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 1, 2, 100, 128, 128, la.BF16)
+    assert f(*args, 4, None) == la.EINVAL
+    assert f(*args, -1, None) == la.EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 1, 2, 100, 96, 128, la.BF16, 3, None) \
+        == la.EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, None, 0, 2, 100, 128, 128, la.BF16, 3, None) \
+        == la.OK  # no sequences: nothing to do

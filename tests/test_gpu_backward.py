@@ -2,9 +2,11 @@
 oracle's gradients.
 
 For L = sum_t <o_t, dO_t> + <S_N, dS_N> the kernel returns dq, dk, dv (bf16)
-and dS_0 (fp32) from three launches of the chunked kernel: dQ as the forward
+and dS_0 (fp32) from the chunked kernel in other roles: dQ as the forward
 prefill of (dO, V, K) from S_0^T, dV and dK as prefills over the reversed
-token order of (K, Q, dO) from dS_N and (V, dO, Q) from dS_N^T.
+token order of (K, Q, dO) from dS_N and (V, dO, Q) from dS_N^T -- run as
+separate passes, as one paired launch, or fused in one sweep
+(``lin_attn_backward_ex``); every strategy is checked.
 
 Gates: max|gpu - oracle| / max|oracle| <= 1e-2 for each of dq, dk, dv, dS_0
 (bf16 inputs and outputs, fp32 accumulation and carried states, the gate of
@@ -25,14 +27,17 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 
 
-def gpu_backward(q, k, v, dO, S0, dSN, block, want_dS0=True):
+STRATEGIES = {"separate": la.BWD_SEPARATE, "paired": la.BWD_PAIRED, "fused": la.BWD_FUSED}
+
+
+def gpu_backward(q, k, v, dO, S0, dSN, block, want_dS0=True, strategy=la.BWD_AUTO):
     qd, kd, vd, dod = (dev(x, "bf16") for x in (q, k, v, dO))
     dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
     B, H, N, d = q.shape
     s0 = None if S0 is None else torch.from_numpy(np.ascontiguousarray(S0, np.float32)).cuda()
     ds = None if dSN is None else torch.from_numpy(np.ascontiguousarray(dSN, np.float32)).cuda()
     ds0 = torch.full((B, H, d, d), float("nan"), device="cuda") if want_dS0 else None
-    la.backward(qd, kd, vd, dod, dq, dk, dv, block, state0=s0, dstate=ds, dstate0=ds0)
+    la.backward(qd, kd, vd, dod, dq, dk, dv, block, state0=s0, dstate=ds, dstate0=ds0, strategy=strategy)
     torch.cuda.synchronize()
     return host(dq), host(dk), host(dv), (host(ds0) if want_dS0 else None)
 
@@ -43,24 +48,26 @@ def grad_inputs(seed, B, H, N, d):
     return q, k, v, dO
 
 
+@pytest.mark.parametrize("strategy", sorted(STRATEGIES))
 @pytest.mark.parametrize("B,H,N,d,block", [
     (1, 2, 1000, 128, 128), (2, 3, 333, 128, 64), (1, 2, 77, 128, 16), (1, 4, 517, 64, 96),
-    (2, 2, 130, 64, 32), (1, 2, 1, 128, 64), (1, 130, 257, 128, 128),
+    (2, 2, 130, 64, 32), (1, 2, 1, 128, 64), (1, 130, 257, 128, 128), (1, 3, 700, 64, 128),
 ])
-def test_backward_random(B, H, N, d, block):
-    announce("backward random", B, H, N, d, block)
+def test_backward_random(B, H, N, d, block, strategy):
+    announce("backward random", B, H, N, d, block, strategy)
     q, k, v, dO = grad_inputs(60 + N, B, H, N, d)
     S0 = random_state(N, (B, H), d)
     dSN = random_state(N + 1, (B, H), d)
     ref = oracle.backward(q, k, v, dO, S0, dSN)
-    got = gpu_backward(q, k, v, dO, S0, dSN, block)
+    got = gpu_backward(q, k, v, dO, S0, dSN, block, strategy=STRATEGIES[strategy])
     errs = [rel_err(g, r) for g, r in zip(got, ref)]
     print("  rel err dq={:.2e} dk={:.2e} dv={:.2e} dS0={:.2e}".format(*errs))
     assert max(errs) <= TOL, errs
 
 
+@pytest.mark.parametrize("strategy", sorted(STRATEGIES))
 @pytest.mark.parametrize("d,N,block", [(128, 300, 128), (128, 77, 32), (64, 129, 64)])
-def test_backward_exact_integers(d, N, block):
+def test_backward_exact_integers(d, N, block, strategy):
     """Sparse {-1, 0, 1} inputs and small integer states: every product and
     partial sum is an integer within bf16's exact range, so the gradients
     are bitwise those of the oracle."""
@@ -77,7 +84,7 @@ def test_backward_exact_integers(d, N, block):
     # the carried states stay in range too
     assert (np.abs(S0) + np.einsum("bhti,bhtj->bhij", np.abs(k), np.abs(v))).max() <= 256
     assert (np.abs(dSN) + np.einsum("bhti,bhtj->bhij", np.abs(q), np.abs(dO))).max() <= 256
-    got = gpu_backward(q, k, v, dO, S0, dSN, block)
+    got = gpu_backward(q, k, v, dO, S0, dSN, block, strategy=STRATEGIES[strategy])
     for name, g, r in zip(("dq", "dk", "dv", "dS0"), got, ref):
         np.testing.assert_array_equal(g, r, err_msg=name)
 
@@ -134,3 +141,38 @@ def test_backward_workload_4x64x32k_sampled():
         errs = [rel_err(g, r) for g, r in zip(got, ref)]
         print(f"  head ({b}, {h}) rel err dq={errs[0]:.2e} dk={errs[1]:.2e} dv={errs[2]:.2e} dS0={errs[3]:.2e}")
         assert max(errs) <= TOL, errs
+
+
+@pytest.mark.parametrize("d,block", [(128, 128), (64, 64), (128, 96)])
+def test_backward_strategies_bitwise_equal(d, block):
+    """The separate, paired and fused strategies compute the same products in
+    the same order (the fused dK role reads the carried state's bf16 copy
+    transposed, which holds the same values as the separate pass's own copy):
+    their gradients agree bitwise, and the default picks one of them."""
+    announce("backward strategies bitwise", d, block)
+    B, H, N = 2, 3, 611
+    q, k, v, dO = grad_inputs(72 + d, B, H, N, d)
+    S0 = random_state(7, (B, H), d)
+    dSN = random_state(8, (B, H), d)
+    runs = {name: gpu_backward(q, k, v, dO, S0, dSN, block, strategy=code) for name, code in STRATEGIES.items()}
+    runs["auto"] = gpu_backward(q, k, v, dO, S0, dSN, block)
+    for name, got in runs.items():
+        for gname, g, r in zip(("dq", "dk", "dv", "dS0"), got, runs["separate"]):
+            np.testing.assert_array_equal(g, r, err_msg=f"{name} {gname}")
+
+
+def test_backward_workload_4x64x32k_fused_vs_separate():
+    """At the headline shape the default runs the fused sweep: every
+    gradient equals the separate passes' bitwise."""
+    announce("backward workload B=4 H=64 N=32768 fused vs separate")
+    B, H, N, d = 4, 64, 32768, 128
+    q, k, v = synth.prefill_inputs_device(13, B, H, N, d)
+    dO = synth.prefill_inputs_device(14, B, H, N, d)[2]
+    outs = {}
+    for name in ("separate", "fused"):
+        g = [torch.empty_like(q) for _ in range(3)] + [torch.empty((B, H, d, d), device="cuda")]
+        la.backward(q, k, v, dO, g[0], g[1], g[2], 128, dstate0=g[3], strategy=STRATEGIES[name])
+        torch.cuda.synchronize()
+        outs[name] = g
+    for gname, a, b in zip(("dq", "dk", "dv", "dS0"), outs["fused"], outs["separate"]):
+        assert torch.equal(a, b), gname
