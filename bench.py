@@ -94,10 +94,10 @@ def backward_bytes(B, H, N, d, **_):
 
 
 def backward_design_bytes(B, H, N, d, **_):
-    """Bytes the two launches move when the dV and dK passes run paired: the
-    dQ pass reads dO, V, K and writes dq (8 d per token-head); the paired
-    launch reads K, V, Q, dO once from HBM (its second reads of Q and dO are
-    served by L2) and writes dk and dv (12 d); plus the fp32 gradient of S_0."""
+    """Bytes the two launches move with the dV and dK passes fused (the
+    default at this shape): the dQ pass reads dO, V, K and writes dq (8 d per
+    token-head); the fused sweep reads K, V, Q, dO once and writes dk and dv
+    (12 d); plus the fp32 gradient of S_0."""
     return B * H * (N * 20 * d + 4 * d * d)
 
 
