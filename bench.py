@@ -344,7 +344,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path shards heads and sequences with no communication, "
-              "and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+              "and the measurement is of a single MI355X; use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -27,8 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lin_attn_oracle.c")
 _LIB = os.path.join(_HERE, "liblin_attn_oracle.so")
 
-# Portable x86-64 baseline with AVX2 (runs on this container's Xeon and on
-# EPYC hosts); no -ffast-math, no FMA contraction, so every product and sum is
+# Portable x86-64 target with AVX2 (runs on current Xeon and EPYC hosts);
+# no -ffast-math, no FMA contraction, so every product and sum is
 # a separately rounded IEEE double operation.
 _CFLAGS = ["-O3", "-std=c11", "-march=x86-64-v3", "-ffp-contract=off",
            "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
