@@ -383,9 +383,11 @@ int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void 
  * block          : as lin_attn_prefill
  *
  * No output may alias an input or another output.
- * Supported: io_dtype BF16, d in {64, 128}, block as for bf16 in
- * lin_attn_prefill.  The products run on bf16 matrix cores with fp32
- * accumulation (the carried states in fp32), as in the forward kernel.
+ * Supported: io_dtype BF16 or F32, d in {64, 128}, block as lin_attn_prefill
+ * allows for that dtype.  With bf16 I/O the products run on bf16 matrix cores
+ * with fp32 accumulation (the carried states in fp32), as in the forward
+ * kernel; with fp32 I/O every product and sum is fp32 on the vector ALUs (the
+ * fp32 prefill kernel in the same roles, three launches).
  */
 int lin_attn_backward(const void *q, const void *k, const void *v, const void *dout,
                       const float *state0, const float *dstate, void *dq, void *dk, void *dv,

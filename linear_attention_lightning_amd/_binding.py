@@ -421,7 +421,8 @@ def backward(q, k, v, dout, dq, dk, dv, block: int, *, state0=None, dstate=None,
              stream=None):
     """Gradients of the chunked prefill (``lin_attn_backward``).
 
-    q, k, v, dout, dq, dk, dv: [B, H, N, d] bf16 (dq, dk, dv written);
+    q, k, v, dout, dq, dk, dv: [B, H, N, d] bf16 or fp32, one dtype (dq, dk,
+    dv written);
     state0 (the forward call's S_0), dstate (gradient of the final state)
     and dstate0 (written: gradient of S_0): [B, H, d, d] fp32 or None."""
     import torch

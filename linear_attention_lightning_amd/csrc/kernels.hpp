@@ -72,6 +72,13 @@ struct PrefillF32Args {
   int blk;
   float *snap;  // as in PrefillArgs
   int snap_every;
+  // gradient passes (grad != 0; state and snap unused): the initial state
+  // from g_in (transposed if g_in_t; null = zero), the final state to g_out
+  // (null = not stored); rev != 0 takes the tokens in reversed order
+  int grad, rev;
+  const float *g_in;
+  int g_in_t;
+  float *g_out;
 };
 int prefill_f32_max_block(int d);
 hipError_t prefill_f32_launch(PrefillF32Args a, int64_t BH, int d, hipStream_t stream);

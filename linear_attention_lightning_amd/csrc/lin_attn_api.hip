@@ -142,9 +142,10 @@ int backward_impl(const void *q, const void *k, const void *v, const void *dout,
   if (B < 0 || H < 0 || N < 0 || d < 0 || block < 0) return LIN_ATTN_EINVAL;
   if (strategy < LIN_ATTN_BWD_AUTO || strategy > LIN_ATTN_BWD_FUSED) return LIN_ATTN_EINVAL;
   if (io_dtype != LIN_ATTN_BF16 && io_dtype != LIN_ATTN_F32) return LIN_ATTN_EUNSUPPORTED;
-  if (io_dtype != LIN_ATTN_BF16) return LIN_ATTN_EUNSUPPORTED;  // the bf16 matrix-core kernel only
   if (d != 64 && d != 128) return LIN_ATTN_EUNSUPPORTED;
-  if (block < 16 || block > lal::prefill_bf16_max_block((int)d) || block % 16 != 0) return LIN_ATTN_EUNSUPPORTED;
+  const bool f32 = io_dtype == LIN_ATTN_F32;
+  const int max_block = f32 ? lal::prefill_f32_max_block((int)d) : lal::prefill_bf16_max_block((int)d);
+  if (block < 16 || block > max_block || block % 16 != 0) return LIN_ATTN_EUNSUPPORTED;
   int64_t BH, total;
   if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &total) || !mul_ok(total, d, &total) || !mul_ok(BH, d * d, &total))
     return LIN_ATTN_EINVAL;
@@ -156,6 +157,30 @@ int backward_impl(const void *q, const void *k, const void *v, const void *dout,
     return LIN_ATTN_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   if (N == 0 && !dstate0) return LIN_ATTN_OK;
+  if (f32) {
+    // fp32 I/O: the three passes on the fp32 kernel (the strategies of the
+    // bf16 path concern its matrix-core kernel; here they all run this way)
+    if (BH > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+    using fp = const float *;
+    lal::PrefillF32Args f{};
+    f.N = N;
+    f.blk = (int)block;
+    f.grad = 1;
+    // dV: reversed prefill of (K, Q, dout) from dS_N, ending in dS_0
+    f.q = (fp)k; f.k = (fp)q; f.v = (fp)dout; f.o = (float *)dv;
+    f.rev = 1; f.g_in = dstate; f.g_in_t = 0; f.g_out = dstate0;
+    hipError_t e = lal::prefill_f32_launch(f, BH, (int)d, s);
+    if (e != hipSuccess || N == 0) return from_hip(e);
+    // dK: reversed prefill of (V, dout, Q) from dS_N^T
+    f.q = (fp)v; f.k = (fp)dout; f.v = (fp)q; f.o = (float *)dk;
+    f.rev = 1; f.g_in = dstate; f.g_in_t = 1; f.g_out = nullptr;
+    e = lal::prefill_f32_launch(f, BH, (int)d, s);
+    if (e != hipSuccess) return from_hip(e);
+    // dQ: forward prefill of (dout, V, K) from S_0^T
+    f.q = (fp)dout; f.k = (fp)v; f.v = (fp)k; f.o = (float *)dq;
+    f.rev = 0; f.g_in = state0; f.g_in_t = 1; f.g_out = nullptr;
+    return from_hip(lal::prefill_f32_launch(f, BH, (int)d, s));
+  }
   int cus = 0;
   const int rc = cu_count(&cus);
   if (rc != LIN_ATTN_OK) return rc;

@@ -11,6 +11,12 @@
 // keep fp32 accuracy.  One workgroup per sequence; the fp32 state, the K and
 // V tiles of the current block, and 16-row slices of Q and P sit in LDS.
 // This path serves small fp32 problems; it is not a throughput kernel.
+//
+// The gradient passes use it in other roles (as the bf16 kernel): the
+// initial state from its own (optionally transposed) buffer, the final state
+// to its own buffer or nowhere, and optionally the tokens in reversed order
+// (logical token t is memory row N-1-t), where the causal mask becomes a
+// suffix sum.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -51,10 +57,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(PrefillF32Args
   const float *kh = a.k + (size_t)bh * (size_t)N * D;
   const float *vh = a.v + (size_t)bh * (size_t)N * D;
   float *oh = a.o + (size_t)bh * (size_t)N * D;
-  float *Sh = a.state + (size_t)bh * D * D;
+  float *Sh = a.grad ? nullptr : a.state + (size_t)bh * D * D;
+  // memory row of logical token t
+  auto mrow = [&](int64_t t) -> size_t { return (size_t)(a.rev ? N - 1 - t : t); };
 
-  for (int idx = tid; idx < D * D; idx += kThreads) Ss[idx] = Sh[idx];
-  const int64_t nsnap = a.snap ? (N / blk) / a.snap_every : 0;
+  if (a.grad) {
+    const float *gi = a.g_in ? a.g_in + (size_t)bh * D * D : nullptr;
+    for (int idx = tid; idx < D * D; idx += kThreads)
+      Ss[idx] = !gi ? 0.f : a.g_in_t ? gi[(idx % D) * D + idx / D] : gi[idx];
+  } else {
+    for (int idx = tid; idx < D * D; idx += kThreads) Ss[idx] = Sh[idx];
+  }
+  const int64_t nsnap = (a.snap && !a.grad) ? (N / blk) / a.snap_every : 0;
 
   for (int64_t tok0 = 0; tok0 < N; tok0 += blk) {
     const int len = (int)((N - tok0) < blk ? (N - tok0) : blk);
@@ -62,14 +76,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(PrefillF32Args
     for (int idx = tid; idx < blk * D; idx += kThreads) {
       const int c = idx / D, i = idx % D;
       const bool ok = c < len;
-      Ks[c * C::KSTR + i] = ok ? kh[(size_t)(tok0 + c) * D + i] : 0.f;
-      Vs[c * D + i] = ok ? vh[(size_t)(tok0 + c) * D + i] : 0.f;
+      Ks[c * C::KSTR + i] = ok ? kh[mrow(tok0 + c) * D + i] : 0.f;
+      Vs[c * D + i] = ok ? vh[mrow(tok0 + c) * D + i] : 0.f;
     }
     for (int rs = 0; rs < len; rs += 16) {
       __syncthreads();  // Ks/Vs staged; previous slice's readers of Qs/Ps done
       for (int idx = tid; idx < 16 * D; idx += kThreads) {
         const int r = idx / D, i = idx % D;
-        Qs[r * C::KSTR + i] = (rs + r < len) ? qh[(size_t)(tok0 + rs + r) * D + i] : 0.f;
+        Qs[r * C::KSTR + i] = (rs + r < len) ? qh[mrow(tok0 + rs + r) * D + i] : 0.f;
       }
       __syncthreads();
       // P[r][c] = q_r . k_c for c <= rs + r (inclusive causal mask), else 0
@@ -89,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(PrefillF32Args
         float intra = 0.f, inter = 0.f;
         for (int c = 0; c <= rs + r; ++c) intra = fmaf(Ps[r * C::PSTR + c], Vs[c * D + j], intra);
         for (int i = 0; i < D; ++i) inter = fmaf(Qs[r * C::KSTR + i], Ss[i * D + j], inter);
-        oh[(size_t)(tok0 + rs + r) * D + j] = intra + inter;
+        oh[mrow(tok0 + rs + r) * D + j] = intra + inter;
       }
     }
     __syncthreads();  // every reader of the old state is done
@@ -109,7 +123,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_f32_kernel(PrefillF32Args
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < D * D; idx += kThreads) Sh[idx] = Ss[idx];
+  if (a.grad) {
+    if (a.g_out)
+      for (int idx = tid; idx < D * D; idx += kThreads) a.g_out[(size_t)bh * D * D + idx] = Ss[idx];
+  } else {
+    for (int idx = tid; idx < D * D; idx += kThreads) Sh[idx] = Ss[idx];
+  }
 }
 
 }  // namespace

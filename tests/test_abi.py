@@ -192,7 +192,8 @@ def test_backward_validation_codes():
     for kw in ({"B": -1}, {"N": -1}, {"block": -1}, {"q": None}, {"dq": None}, {"q": MISALIGNED},
                {"s0": MISALIGNED}, {"ds": MISALIGNED}, {"ds0": MISALIGNED}, {"B": 1 << 40, "H": 1 << 30}):
         assert bwd(**kw) == la.EINVAL, kw
-    for kw in ({"io": la.F32}, {"io": 9}, {"d": 96}, {"block": 144}, {"block": 8}, {"block": 40}):
+    for kw in ({"io": 9}, {"d": 96}, {"block": 144}, {"block": 8}, {"block": 40},
+               {"io": la.F32, "block": 128}):  # fp32 I/O: blocks up to 64 at d = 128
         assert bwd(**kw) == la.EUNSUPPORTED, kw
     assert bwd(B=0, q=None, dq=None) == la.OK
     assert bwd(N=0, q=None, dq=None) == la.OK  # no tokens and no dS_0 requested: nothing to do

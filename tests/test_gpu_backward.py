@@ -10,7 +10,8 @@ separate passes, as one paired launch, or fused in one sweep
 
 Gates: max|gpu - oracle| / max|oracle| <= 1e-2 for each of dq, dk, dv, dS_0
 (bf16 inputs and outputs, fp32 accumulation and carried states, the gate of
-the bf16 forward path); bitwise for exact-integer inputs.
+the bf16 forward path), <= 1e-4 with fp32 inputs and outputs (the fp32
+kernel in the same roles); bitwise for exact-integer inputs.
 """
 import numpy as np
 import pytest
@@ -30,8 +31,8 @@ TOL = 1e-2
 STRATEGIES = {"separate": la.BWD_SEPARATE, "paired": la.BWD_PAIRED, "fused": la.BWD_FUSED}
 
 
-def gpu_backward(q, k, v, dO, S0, dSN, block, want_dS0=True, strategy=la.BWD_AUTO):
-    qd, kd, vd, dod = (dev(x, "bf16") for x in (q, k, v, dO))
+def gpu_backward(q, k, v, dO, S0, dSN, block, want_dS0=True, strategy=la.BWD_AUTO, dtype="bf16"):
+    qd, kd, vd, dod = (dev(x, dtype) for x in (q, k, v, dO))
     dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
     B, H, N, d = q.shape
     s0 = None if S0 is None else torch.from_numpy(np.ascontiguousarray(S0, np.float32)).cuda()
@@ -176,3 +177,45 @@ def test_backward_workload_4x64x32k_fused_vs_separate():
         outs[name] = g
     for gname, a, b in zip(("dq", "dk", "dv", "dS0"), outs["fused"], outs["separate"]):
         assert torch.equal(a, b), gname
+
+
+@pytest.mark.parametrize("B,H,N,d,block", [
+    (1, 2, 300, 128, 64), (2, 3, 129, 64, 128), (1, 2, 77, 128, 16), (1, 1, 1, 64, 32), (1, 4, 1000, 64, 64),
+])
+def test_backward_fp32(B, H, N, d, block):
+    """fp32 inputs and outputs: the fp32 kernel in the gradient roles, gated
+    at 1e-4 like the fp32 forward path."""
+    announce("backward fp32", B, H, N, d, block)
+    rng = np.random.default_rng([80, N, d])
+    q, k, v, dO = (rng.standard_normal((B, H, N, d)).astype(np.float32) * s
+                   for s in (d ** -0.5, d ** -0.5, 1.0, 1.0))
+    S0 = random_state(N + 2, (B, H), d)
+    dSN = random_state(N + 3, (B, H), d)
+    ref = oracle.backward(q, k, v, dO, S0, dSN)
+    got = gpu_backward(q, k, v, dO, S0, dSN, block, dtype="fp32")
+    errs = [rel_err(g, r) for g, r in zip(got, ref)]
+    print("  rel err dq={:.2e} dk={:.2e} dv={:.2e} dS0={:.2e}".format(*errs))
+    assert max(errs) <= 1e-4, errs
+
+
+def test_backward_fp32_exact_integers_and_edges():
+    """Exact integers give the oracle's gradients bitwise; NULL states mean
+    zero; with no tokens dS_0 = dS_N."""
+    announce("backward fp32 exact integers / edges")
+    B, H, N, d = 1, 3, 150, 64
+    q, k, v = synth.integer_inputs(990, B, H, N, d)
+    dO, _, _ = synth.integer_inputs(991, B, H, N, d)
+    rng = np.random.default_rng(92)
+    S0 = rng.integers(-2, 3, (B, H, d, d)).astype(np.float64)
+    dSN = rng.integers(-2, 3, (B, H, d, d)).astype(np.float64)
+    ref = oracle.backward(q, k, v, dO, S0, dSN)
+    got = gpu_backward(q, k, v, dO, S0, dSN, 64, dtype="fp32")
+    for name, g, r in zip(("dq", "dk", "dv", "dS0"), got, ref):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+    ref0 = oracle.backward(q, k, v, dO, None, None)
+    got0 = gpu_backward(q, k, v, dO, None, None, 64, dtype="fp32")
+    for name, g, r in zip(("dq", "dk", "dv", "dS0"), got0, ref0):
+        np.testing.assert_array_equal(g, r, err_msg=name)
+    e = np.zeros((B, H, 0, d), np.float32)
+    _, _, _, dS0 = gpu_backward(e, e, e, e, None, dSN, 64, dtype="fp32")
+    np.testing.assert_array_equal(dS0, dSN)
