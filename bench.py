@@ -234,13 +234,25 @@ def decode_steps(la, synth, torch, reps: int = 5):
         torch.cuda.synchronize()
         same = same and torch.equal(S, S_ref)
     graph_ms = timed(graph.replay)
+    # the same 128 steps with the state stored in bf16 (the precision hazard
+    # of a low-precision stored state): error of its final state and of its
+    # outputs against the fp32-state run
+    S16 = S0.to(torch.bfloat16)
+    o16 = torch.empty_like(o)
+    for t in range(DECODE_STEPS):
+        la.decode(qs[t], ks[t], vs[t], o16[t], S16)
+    torch.cuda.synchronize()
+    s_err = ((S16.float() - S_ref).abs().max() / S_ref.abs().max()).item()
+    o_err = ((o16.float() - o_ref.float()).abs().max() / o_ref.float().abs().max()).item()
     step_bytes = decode_bytes(D["B"], D["H"], D["d"], 4)
     return {"steps": DECODE_STEPS,
             "eager_ms": eager_ms, "eager_ms_per_step": eager_ms / DECODE_STEPS,
             "graph_ms": graph_ms, "graph_ms_per_step": graph_ms / DECODE_STEPS,
             "graph_GBps": step_bytes * DECODE_STEPS / (graph_ms / 1e3) / 1e9,
             "graph_pct_hbm_peak": 100 * step_bytes * DECODE_STEPS / (graph_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
-            "graph_replays_bitwise_equal_to_eager": bool(same)}
+            "graph_replays_bitwise_equal_to_eager": bool(same),
+            "bf16_state_vs_fp32_state_rel_err_after_128_steps": s_err,
+            "bf16_state_outputs_vs_fp32_state_outputs_rel_err": o_err}
 
 
 def long_context(la, synth, torch, steps: int = 5):
@@ -557,6 +569,7 @@ def main():
         },
         "prefill": {
             "ms": avg["prefill"], "ms_min": best["prefill"],
+            "ms_median": sorted(kern_ms["prefill"])[len(kern_ms["prefill"]) // 2],
             "tokens_per_s": tokens / p_s,
             "tflops_useful": p_flops / p_s / 1e12,
             "tflops_dense_tile": p_dense / p_s / 1e12,
