@@ -24,16 +24,22 @@
 //    double-buffered: block b+1 streams in while block b is computed.  The
 //    buffer descriptor covers exactly the valid rows, so rows past the end of
 //    the sequence arrive as zeros -- ragged tails need no other masking.
-//  * Q rows are loaded by each wave straight into the registers that feed the
-//    matrix cores, one block ahead.
+//  * Q rows are loaded by each wave into registers one block ahead, as whole
+//    128-byte lines (one L1 request per line), and rearranged into the
+//    matrix-core operand layout by a masked DPP row rotation; the head
+//    dimension is contracted in the chunk order that this layout gives, for
+//    all operands alike.
+//  * K, V and Q are read once, with the non-temporal cache policy.
 //  * LDS tiles are unpadded with an XOR swizzle of their 16-byte chunks,
 //    chosen so that 16-byte fragment reads (one row per lane) and the
 //    transposing 8-byte reads both run without bank conflicts.
 //
 // Products (all v_mfma_f32_16x16x32_bf16).  Outputs are computed transposed,
 // O^T = S^T Q^T + V^T P^T, so a lane holds four consecutive value features of
-// one token and stores 8 bytes.  P^T = K Q^T lands directly in the B-operand
-// layout of V^T P^T.  K^T and V are read token-major with ds_read_b64_tr_b16.
+// one token; lane swaps across value tiles (permlane32/16 swaps, a DPP row
+// rotation) turn them into 16-byte stores that write whole 128-byte lines.
+// P^T = K Q^T lands directly in the B-operand layout of V^T P^T.  K^T and V
+// are read token-major with ds_read_b64_tr_b16.
 //
 // Balance.  Phase A (outputs) pairs row tiles t and NT-1-t so that every
 // wave has the same causal work, and splits value columns across the waves
@@ -48,7 +54,11 @@
 // sums -- the reverse-carried state of the gradients.  Every buffer offset
 // of a row stays in the per-lane offset register; rows past the block's end
 // get negative offsets, which lie outside the buffer descriptor, so they
-// read zeros and their stores are dropped, as in forward order.
+// read zeros and their stores are dropped, as in forward order.  The dV and
+// dK passes of the gradients share their keys and values (q and dout,
+// swapped) and their carried states (G and G^T): kPsGradRevPair runs both
+// passes in one launch with a sequence's two workgroups on one XCD, and
+// kPsGradFused runs both in one workgroup that stages each tile once.
 //
 // State storage (template parameter SM).  The state that enters and leaves
 // the kernel is fp32, optionally with snapshots of it every few blocks (a
@@ -67,10 +77,7 @@
 namespace lal {
 namespace {
 
-#ifndef LAL_PREFILL_WAVES
-#define LAL_PREFILL_WAVES 4
-#endif
-constexpr int kWaves = LAL_PREFILL_WAVES;
+constexpr int kWaves = 4;  // one per SIMD, each with the whole register file
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlkMax = 128;
 
