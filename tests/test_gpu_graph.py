@@ -3,8 +3,9 @@
 Every entry point only validates its arguments and enqueues kernels on the
 caller's stream (no allocation, no memset, no synchronisation), so a caller
 may capture a sequence of calls in a HIP graph and replay it.  These tests
-capture decode steps, a prefill, the sequence-split prefill and the split
-state accumulation, replay each graph several times with eager work and
+capture decode steps, a prefill, the sequence-split prefill, the split
+state accumulation, the fused backward, speculative verify and commit and
+a scaled E4M3 decode, replay each graph several times with eager work and
 synchronisations between the replays, and require every replay to equal the
 eagerly launched result bitwise.
 """
@@ -17,6 +18,12 @@ from linear_attention_lightning_amd import synth
 from gpu_helpers import announce
 
 pytestmark = pytest.mark.gpu
+
+
+def same(a, b):
+    if a.dtype == torch.float8_e4m3fn:
+        return torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    return torch.equal(a, b)
 
 
 def replay_check(run, outputs, reset):
@@ -36,18 +43,21 @@ def replay_check(run, outputs, reset):
     for i in range(3):
         # poison every output, then restore the inputs the run reads (states)
         for t in outputs:
-            t.fill_(float("nan"))
+            if t.dtype == torch.float8_e4m3fn:
+                t.view(torch.uint8).fill_(0x7f)  # E4M3 NaN
+            else:
+                t.fill_(float("nan"))
         reset()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         for t, r in zip(outputs, ref):
-            assert torch.equal(t, r), f"replay {i} differs from the eager run"
+            assert same(t, r), f"replay {i} differs from the eager run"
         reset()
         run()
         torch.cuda.synchronize()
         for t, r in zip(outputs, ref):
-            assert torch.equal(t, r), f"eager run after replay {i} differs"
+            assert same(t, r), f"eager run after replay {i} differs"
 
 
 def test_graph_decode_steps():
@@ -90,3 +100,41 @@ def test_graph_prefill_and_seqsplit():
         la.state_accumulate_split(k, v, dS, ws_s)
 
     replay_check(run, [o1, S1, o2, S2, dS], reset)
+
+
+def test_graph_backward_and_speculative():
+    announce("graph: fused backward, speculative verify/commit, scaled E4M3 decode")
+    B, H, N, d = 1, 4, 1000, 128
+    q, k, v = synth.prefill_inputs_device(32, B, H, N, d)
+    dO = synth.prefill_inputs_device(33, B, H, N, d)[2]
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ds0 = torch.empty((B, H, d, d), device="cuda")
+    dSN = torch.randn((B, H, d, d), generator=torch.Generator(device="cuda").manual_seed(33), device="cuda")
+
+    def run_bwd():
+        la.backward(q, k, v, dO, dq, dk, dv, 128, dstate=dSN, dstate0=ds0, strategy=la.BWD_FUSED)
+
+    replay_check(run_bwd, [dq, dk, dv, ds0], lambda: None)
+
+    Bd, Hd, T = 8, 4, 4
+    S0 = synth.decode_initial_state_device(Bd, Hd, d, n_outer=64)
+    tq, tk, tv = synth.prefill_inputs_device(34, Bd, Hd, T, d)
+    to = torch.empty_like(tq)
+    acc = torch.tensor([3, 0, 4, 1, 2, 4, 3, 1], dtype=torch.int32, device="cuda")
+    S = S0.clone()
+    scale = torch.exp2(torch.ceil(torch.log2(S0.abs().amax(dim=(2, 3)) / 224.0)))
+    S8_0 = (S0 / scale[:, :, None, None]).to(torch.float8_e4m3fn)
+    S8 = S8_0.clone()
+    dq1, dk1, dv1 = synth.decode_step_inputs_device(3, Bd, Hd, d)
+    o1 = torch.empty_like(dq1)
+
+    def run_spec():
+        la.decode_verify(tq, tk, tv, to, S)
+        la.decode_commit(tk, tv, S, acc)
+        la.decode(dq1, dk1, dv1, o1, S8, state_scale=scale)
+
+    def reset():
+        S.copy_(S0)
+        S8.copy_(S8_0)
+
+    replay_check(run_spec, [to, S, o1, S8], reset)
