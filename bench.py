@@ -39,6 +39,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import itertools
 import json
 import os
 import re
@@ -302,42 +303,48 @@ def hbm_ceiling(torch, reps: int = 5):
     non-temporal loads, consecutive lanes at consecutive addresses, one
     contiguous run of 4 KiB units per workgroup.  Measured for reads only,
     for 3 bytes read per byte written (the prefill's mix: q, k, v in, o out)
-    and for 1:1 (the decode step's state read and write), each the best
-    average over grid sizes and store policies.  HIP events on the launch
+    and for 1:1, between two buffers and in place (the decode step reads and
+    writes its state in place), each the best average over grid sizes and
+    store policies, and over 1, 4 or 16 units loaded per wave before their
+    stores.  HIP events on the launch
     stream, `reps` timed launches after 2 untimed ones."""
     lib = ctypes.CDLL(PROBE_LIB)
     lib.hbm_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     read_bytes = 6 << 30
     src = torch.ones(read_bytes // 4, dtype=torch.int32, device=dev)
     dst = torch.zeros(3 << 28, dtype=torch.int32, device=dev)  # 3 GiB
     unit = 4096
-    mixes = {"read_only": (1, 0, read_bytes // unit), "r3w1": (3, 1, read_bytes // (3 * unit)),
-             "r1w1": (1, 1, (3 << 30) // unit)}
+    mixes = {"read_only": (1, 0, read_bytes // unit, False), "r3w1": (3, 1, read_bytes // (3 * unit), False),
+             "r1w1": (1, 1, (3 << 30) // unit, False),
+             # in place: each 16-byte piece read and written back to the same
+             # address, the access pattern of a state read-modify-write
+             "r1w1_in_place": (1, 1, (3 << 30) // unit, True)}
     out = {}
-    for name, (rd, wr, units) in mixes.items():
+    for name, (rd, wr, units, in_place) in mixes.items():
         moved = units * unit * (rd + wr)
         best = None
-        for nt in ((0, 1) if wr else (0,)):
-            for wgs in (2048, 8192, 16384):
-                ms = []
-                for i in range(reps + 2):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    rc = lib.hbm_stream(src.data_ptr(), dst.data_ptr(), units, rd, wr, nt, wgs, stream.cuda_stream)
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    if rc != 0:
-                        raise RuntimeError(f"hbm_stream returned {rc}")
-                    if i >= 2:
-                        ms.append(e0.elapsed_time(e1))
-                gbs = moved / (sum(ms) / len(ms) / 1e3) / 1e9
-                if best is None or gbs > best[0]:
-                    best = (gbs, nt, wgs)
+        for nt, wgs, batch in itertools.product((0, 1) if wr else (0,), (2048, 8192, 16384), (1, 4, 16)):
+            ms = []
+            for i in range(reps + 2):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                target = src if in_place else dst
+                rc = lib.hbm_stream(src.data_ptr(), target.data_ptr(), units, rd, wr, nt, wgs, batch,
+                                    stream.cuda_stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if rc != 0:
+                    raise RuntimeError(f"hbm_stream returned {rc}")
+                if i >= 2:
+                    ms.append(e0.elapsed_time(e1))
+            gbs = moved / (sum(ms) / len(ms) / 1e3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, nt, wgs, batch)
         out[name + "_GBps"] = best[0]
-        out[name + "_config"] = f"nt_store={best[1]} workgroups={best[2]}"
+        out[name + "_config"] = f"nt_store={best[1]} workgroups={best[2]} batch={best[3]}"
     del src, dst
     out["kernel"] = "plain streaming kernel, 16-byte non-temporal loads, 256-lane workgroups (csrc/hbm_stream.hip)"
     return out
@@ -604,6 +611,8 @@ def main():
             "tokens_per_s_fp32_state": D["B"] / (avg["decode_fp32"] / 1e3),
             "fp32_state_pct_of_1to1_stream_ceiling": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9
             / ceiling["r1w1_GBps"],
+            "fp32_state_pct_of_in_place_1to1_stream_ceiling": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9
+            / ceiling["r1w1_in_place_GBps"],
             "steps_128": steps128,
             "speculative": {
                 "drafts": DRAFTS, "accepted": DRAFTS - 1,

@@ -2,7 +2,8 @@
  * library, built separately as libhbm_stream.so).
  *
  * hbm_stream: one launch of a plain streaming kernel on `stream`.
- *   src, dst      device pointers, 16-byte aligned, owned by the caller.
+ *   src, dst      device pointers, 16-byte aligned, owned by the caller; with
+ *                 one read per write they may be equal (an in-place stream).
  *   units         work units of 4096 bytes per read slice: the kernel reads
  *                 units * reads_per_write * 4096 bytes of src and, when
  *                 `write` is non-zero, writes units * 4096 bytes of dst
@@ -11,6 +12,7 @@
  *   reads_per_write  1 or 3 with writes, 1 without.
  *   nt_store      non-zero: non-temporal stores.
  *   workgroups    workgroups of 256 lanes, each taking a contiguous run of units.
+ *   batch         1, 4 or 16: units each wave loads before it stores them.
  * Returns 0, -1 for a null pointer or a bad size, -2 for an unsupported
  * combination, -3 for a launch error.
  */
@@ -25,7 +27,7 @@ extern "C" {
 #endif
 
 int hbm_stream(const void *src, void *dst, int64_t units, int reads_per_write, int write, int nt_store,
-               int workgroups, hipStream_t stream);
+               int workgroups, int batch, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -7,8 +7,12 @@
 //
 // Work is cut into units of 256 lanes x 16 bytes.  A unit reads RD such
 // slices (16-byte non-temporal loads, consecutive lanes at consecutive
-// addresses) and, when RD > 0 and writes are on, writes one slice of their
-// XOR.  Each workgroup takes a contiguous run of units.
+// addresses) and, when writes are on, writes one slice of their XOR.  Each
+// workgroup takes a contiguous run of units and walks it BATCH units at a
+// time: all loads of a batch are issued before its stores, so a wave keeps
+// BATCH * RD loads in flight.  With one read per write, source and
+// destination may be the same buffer: each lane then writes its slice back
+// to the address it read (a read-modify-write stream).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -19,25 +23,49 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int RD, bool WRITE, bool NT_STORE>
-__global__ __launch_bounds__(256) void stream_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
-                                                      int64_t units, int64_t per_wg) {
+template <bool NT_STORE>
+__device__ __forceinline__ void put(u32x4 *p, u32x4 x) {
+  if constexpr (NT_STORE)
+    __builtin_nontemporal_store(x, p);
+  else
+    *p = x;
+}
+
+// `salt` is zero at run time.  Writing back the loaded value unchanged would
+// let the compiler drop an in-place stream's stores and loads.
+template <int RD, bool WRITE, bool NT_STORE, int BATCH>
+__device__ __forceinline__ void stream_run(const u32x4 *src, u32x4 *dst, int64_t units, int64_t per_wg,
+                                           unsigned salt) {
   const int64_t u0 = (int64_t)blockIdx.x * per_wg;
   const int64_t u1 = u0 + per_wg < units ? u0 + per_wg : units;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (int64_t u = u0; u < u1; ++u) {
+  int64_t u = u0;
+  for (; u + BATCH <= u1; u += BATCH) {
+    u32x4 x[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const u32x4 *s = src + (u + b) * RD * 256 + threadIdx.x;
+      x[b] = u32x4{salt, salt, salt, salt};
+#pragma unroll
+      for (int r = 0; r < RD; ++r) x[b] ^= __builtin_nontemporal_load(s + r * 256);
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      if constexpr (WRITE)
+        put<NT_STORE>(dst + (u + b) * 256 + threadIdx.x, x[b]);
+      else
+        acc ^= x[b];
+    }
+  }
+  for (; u < u1; ++u) {  // the run's last units, fewer than a batch
     const u32x4 *s = src + u * RD * 256 + threadIdx.x;
-    u32x4 x = {0u, 0u, 0u, 0u};
+    u32x4 x = {salt, salt, salt, salt};
 #pragma unroll
     for (int r = 0; r < RD; ++r) x ^= __builtin_nontemporal_load(s + r * 256);
-    if constexpr (WRITE) {
-      if constexpr (NT_STORE)
-        __builtin_nontemporal_store(x, dst + u * 256 + threadIdx.x);
-      else
-        dst[u * 256 + threadIdx.x] = x;
-    } else {
+    if constexpr (WRITE)
+      put<NT_STORE>(dst + u * 256 + threadIdx.x, x);
+    else
       acc ^= x;
-    }
   }
   // read-only runs keep their loads alive through a store that never happens
   // for the fill patterns used (all bytes equal give acc[0] == acc[1])
@@ -45,27 +73,56 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4 *__restrict__ s
     if (acc[0] != acc[1]) dst[threadIdx.x] = acc;
 }
 
-template <int RD, bool WRITE, bool NT>
+template <int RD, bool WRITE, bool NT_STORE, int BATCH>
+__global__ __launch_bounds__(256) void stream_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                      int64_t units, int64_t per_wg, unsigned salt) {
+  stream_run<RD, WRITE, NT_STORE, BATCH>(src, dst, units, per_wg, salt);
+}
+
+// the in-place stream: one pointer, no aliasing promise
+template <bool NT_STORE, int BATCH>
+__global__ __launch_bounds__(256) void in_place_kernel(u32x4 *buf, int64_t units, int64_t per_wg,
+                                                       unsigned salt) {
+  stream_run<1, true, NT_STORE, BATCH>(buf, buf, units, per_wg, salt);
+}
+
+template <int RD, bool WRITE, bool NT, int BATCH>
 void launch(const void *src, void *dst, int64_t units, int wgs, hipStream_t stream) {
   const int64_t per = (units + wgs - 1) / wgs;
-  stream_kernel<RD, WRITE, NT><<<wgs, 256, 0, stream>>>((const u32x4 *)src, (u32x4 *)dst, units, per);
+  if (src == dst)
+    in_place_kernel<NT, BATCH><<<wgs, 256, 0, stream>>>((u32x4 *)dst, units, per, 0u);
+  else
+    stream_kernel<RD, WRITE, NT, BATCH><<<wgs, 256, 0, stream>>>((const u32x4 *)src, (u32x4 *)dst, units, per, 0u);
+}
+
+template <int BATCH>
+int dispatch(const void *src, void *dst, int64_t units, int rd, int write, int nt, int wgs, hipStream_t stream) {
+  if (rd == 1 && write)
+    nt ? launch<1, true, true, BATCH>(src, dst, units, wgs, stream)
+       : launch<1, true, false, BATCH>(src, dst, units, wgs, stream);
+  else if (rd == 3 && write)
+    nt ? launch<3, true, true, BATCH>(src, dst, units, wgs, stream)
+       : launch<3, true, false, BATCH>(src, dst, units, wgs, stream);
+  else if (rd == 1 && !write)
+    launch<1, false, false, BATCH>(src, dst, units, wgs, stream);
+  else
+    return -2;
+  return 0;
 }
 
 }  // namespace
 
 extern "C" int hbm_stream(const void *src, void *dst, int64_t units, int reads_per_write, int write,
-                          int nt_store, int workgroups, hipStream_t stream) {
+                          int nt_store, int workgroups, int batch, hipStream_t stream) {
   if (!src || !dst || units < 0 || workgroups <= 0) return -1;
+  if (batch != 1 && batch != 4 && batch != 16) return -2;
+  if (src == dst && !(reads_per_write == 1 && write)) return -2;
+  if (reads_per_write != 1 && !(reads_per_write == 3 && write)) return -2;
   if (units == 0) return 0;
-  if (reads_per_write == 1 && write)
-    nt_store ? launch<1, true, true>(src, dst, units, workgroups, stream)
-             : launch<1, true, false>(src, dst, units, workgroups, stream);
-  else if (reads_per_write == 3 && write)
-    nt_store ? launch<3, true, true>(src, dst, units, workgroups, stream)
-             : launch<3, true, false>(src, dst, units, workgroups, stream);
-  else if (reads_per_write == 1 && !write)
-    launch<1, false, false>(src, dst, units, workgroups, stream);
-  else
-    return -2;
+  const int rc =
+      batch == 1   ? dispatch<1>(src, dst, units, reads_per_write, write, nt_store, workgroups, stream)
+      : batch == 4 ? dispatch<4>(src, dst, units, reads_per_write, write, nt_store, workgroups, stream)
+                   : dispatch<16>(src, dst, units, reads_per_write, write, nt_store, workgroups, stream);
+  if (rc) return rc;
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }

@@ -289,10 +289,13 @@ def test_stream_probe_is_a_separate_library():
     probe = os.path.join(os.path.dirname(la.LIB_PATH), "libhbm_stream.so")
     lib = ctypes.CDLL(probe)
     lib.hbm_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                               ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    assert lib.hbm_stream(None, FAKE, 1, 1, 1, 0, 1, None) == -1
-    assert lib.hbm_stream(FAKE, FAKE, -1, 1, 1, 0, 1, None) == -1
-    assert lib.hbm_stream(FAKE, FAKE, 0, 3, 1, 0, 1, None) == 0  # nothing to do: no launch
+                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.hbm_stream(None, FAKE, 1, 1, 1, 0, 1, 1, None) == -1
+    assert lib.hbm_stream(FAKE, FAKE, -1, 1, 1, 0, 1, 1, None) == -1
+    assert lib.hbm_stream(FAKE, FAKE, 0, 1, 1, 0, 1, 1, None) == 0  # nothing to do: no launch
+    assert lib.hbm_stream(FAKE, FAKE, 1, 3, 1, 0, 1, 1, None) == -2  # in place needs one read per write
+    assert lib.hbm_stream(FAKE, FAKE, 1, 1, 0, 0, 1, 1, None) == -2  # an in-place run must write
+    assert lib.hbm_stream(FAKE, FAKE, 1, 1, 1, 0, 1, 2, None) == -2  # batch is 1, 4 or 16
     nm = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True, check=True)
     assert "hbm_stream" not in nm.stdout
 
