@@ -5,8 +5,10 @@
 //  verify:  o_t = q_t^T S_t for t = 0 .. T-1, S_t = S + sum_{s <= t} k_s v_s^T,
 //           without writing the state (the recurrence of "MiniMax-M1で理解する"
 //           (zenn.dev/liushuzhi), section "線形アテンションの数学的基礎",
-//           unrolled over the drafts): each state row is read once and
-//           carried through the drafts in registers;
+//           unrolled over the drafts), split as
+//           o_t = q_t^T S + sum_{s <= t} (q_t . k_s) v_s: one pass over the
+//           state with one multiply-add per state element and draft, plus
+//           the drafts' T x T table of q_t . k_s;
 //  commit:  S <- S + sum_{t < a} k_t v_t^T for the a drafts accepted by the
 //           sequence (a = 0 leaves S as it was: the rollback).
 //
@@ -14,9 +16,10 @@
 // verifying T drafts costs about one decode step of state traffic instead of
 // T.  Layout as in the one-token decode: one wavefront per (batch, head),
 // each lane owns 4 columns of the rows it walks (16-byte fp32 or 8-byte bf16
-// state accesses); q and k of the drafts are staged in LDS (transposed, so a
-// state row's T multipliers are contiguous), and each lane keeps its columns
-// of the drafts' v in registers.
+// state accesses).  verify stages q and k of the drafts in LDS (transposed,
+// so a state row's multipliers are contiguous), multiplies every draft with
+// no per-draft branch, and reads its columns of the drafts' v only for the
+// table term; commit keeps its columns of v in registers.
 //
 // commit applies, per state element, the same fused multiply-adds in the
 // same order as T one-token decode steps; with an fp32 state the result is
@@ -24,6 +27,8 @@
 // at the store.  Narrow states carry a per-sequence scale and are kept in
 // stored units (state / scale) as in the one-token decode: verify multiplies
 // the state part of its outputs by the scale, commit divides v by it.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -80,10 +85,17 @@ __device__ __forceinline__ void st_state4(void *row, int cg, const float (&s)[4]
   }
 }
 
-// verify, with TM >= T drafts of room.  Per state row i each lane carries
-// c = S[i][cols] + sum_{s <= t} k_s[i] v_s[cols] through the drafts t and
-// adds q_t[i] c to output t: o_t = q_t^T S_t term by term, one pass over the
-// state and no separate q_t . k_s products.
+// LDS bytes per verify wave: q^T of TM drafts in fp32, k^T in the I/O type
+// (it feeds only the table), and the TM x TM table of q_t . k_s
+template <int D, int TM, bool IO_BF16>
+constexpr size_t verify_lds_bytes() {
+  return 4 * (size_t)D * TM + (IO_BF16 ? 2 : 4) * (size_t)D * TM + 4 * (size_t)TM * TM;
+}
+
+// verify, with TM >= T drafts of room.  Per state row i each lane adds
+// q_t[i] S[i][cols] to output t (the state part), then the lanes build the
+// table P[t][s] = q_t . k_s together and each adds sum_{s <= t} P[t][s] v_s
+// for its columns (the drafts' own part).
 template <int D, bool IO_BF16, int ST, int TM>
 __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   constexpr int ES = ST == kStF32 ? 4 : ST == kStBF16 ? 2 : 1;
@@ -99,60 +111,67 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   const int T = a.T;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  float *qT = lds + (size_t)wave * 2 * D * TM;  // qT[i * TM + t]
-  float *kT = qT + D * TM;                      // kT[i * TM + t]
+  using KT = std::conditional_t<IO_BF16, u16, float>;  // bf16 bits or fp32
+  char *wl = (char *)lds + (size_t)wave * verify_lds_bytes<D, TM, IO_BF16>();
+  float *qT = (float *)wl;                                     // qT[i * TM + t]
+  KT *kT = (KT *)(wl + 4 * (size_t)D * TM);                    // kT[i * TM + t]
+  float *P = (float *)(wl + (4 + sizeof(KT)) * (size_t)D * TM);  // P[t * TM + s] = q_t . k_s
   const int64_t h = (int64_t)blockIdx.x * kWV + wave;
   const bool valid = h < a.BH;
   const int cg = lane % LPR, rph = lane / LPR;
+  const char *Sh = (const char *)a.state + (size_t)(valid ? h : 0) * D * D * ES;
+  auto load_rows = [&](float(&s)[U][4], int m0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) ld_state4<ST>(Sh + (size_t)(rph + RP * (m0 + u)) * D * ES, cg, s[u]);
+  };
 
-  float vr[TM][4];  // this lane's 4 columns of every draft's v
-#pragma unroll
-  for (int t = 0; t < TM; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vr[t][e] = 0.f;
   if (valid) {
-    // q and k of the drafts, transposed into LDS: every 16-byte load is
-    // issued before the first store (the stores wait on them)
+    // q and k of the drafts, transposed into LDS, in groups of at most 4
+    // 16-byte pieces per lane: every load of a group is issued before its
+    // first store (the stores wait on them)
     const int npieces = D * T / EPC;
     const char *qb = (const char *)a.q + (size_t)h * T * D * (IO_BF16 ? 2 : 4);
     const char *kb = (const char *)a.k + (size_t)h * T * D * (IO_BF16 ? 2 : 4);
-    u32x4 qp[NP], kp[NP];
+    constexpr int NG = NP < 4 ? NP : 4;
+    static_assert(NP % NG == 0, "piece groups");
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int c = lane + 64 * j;
-      if (c < npieces) {
-        qp[j] = *(const u32x4 *)(qb + (size_t)c * 16);
-        kp[j] = *(const u32x4 *)(kb + (size_t)c * 16);
-      }
-    }
+    for (int j0 = 0; j0 < NP; j0 += NG) {
+      u32x4 qp[NG], kp[NG];
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      if (t < T) {
-        const size_t base = ((size_t)h * T + t) * D + 4 * cg;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vr[t][e] = ld_io<IO_BF16>(a.v, base + e);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int c = lane + 64 * j;
-      if (c < npieces) {
-        const int t = c * EPC / D, i0 = c * EPC % D;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          float qv, kv;
-          if constexpr (IO_BF16) {
-            const uint32_t wq = qp[j][e / 2], wk = kp[j][e / 2];
-            qv = __uint_as_float(e & 1 ? wq & 0xffff0000u : wq << 16);
-            kv = __uint_as_float(e & 1 ? wk & 0xffff0000u : wk << 16);
-          } else {
-            qv = __uint_as_float(qp[j][e]);
-            kv = __uint_as_float(kp[j][e]);
-          }
-          qT[(i0 + e) * TM + t] = qv;
-          kT[(i0 + e) * TM + t] = kv;
+      for (int j = 0; j < NG; ++j) {
+        const int c = lane + 64 * (j0 + j);
+        if (c < npieces) {
+          qp[j] = *(const u32x4 *)(qb + (size_t)c * 16);
+          kp[j] = *(const u32x4 *)(kb + (size_t)c * 16);
         }
       }
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const int c = lane + 64 * (j0 + j);
+        if (c < npieces) {
+          const int t = c * EPC / D, i0 = c * EPC % D;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            float qv;
+            KT kv;
+            if constexpr (IO_BF16) {
+              const uint32_t wq = qp[j][e / 2], wk = kp[j][e / 2];
+              qv = __uint_as_float(e & 1 ? wq & 0xffff0000u : wq << 16);
+              kv = (u16)(e & 1 ? wk >> 16 : wk & 0xffffu);
+            } else {
+              qv = __uint_as_float(qp[j][e]);
+              kv = __uint_as_float(kp[j][e]);
+            }
+            qT[(i0 + e) * TM + t] = qv;
+            kT[(i0 + e) * TM + t] = kv;
+          }
+        }
+      }
+    }
+    // q of the drafts past T reads as zero in the state pass
+    if (T < TM) {
+      const int rest = TM - T;
+      for (int c = lane; c < D * rest; c += 64) qT[(c / rest) * TM + T + c % rest] = 0.f;
     }
   }
   __syncthreads();
@@ -166,39 +185,37 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[t][e] = 0.f;
 
-  const char *Sh = (const char *)a.state + (size_t)h * D * D * ES;
-  for (int m0 = 0; m0 < RPL; m0 += U) {
-    float s[U][4];
+  // q of row i for all TM drafts, as TM / 4 float4 LDS reads
+  auto read_q = [&](f32x4(&q)[TM / 4], int i) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) ld_state4<ST>(Sh + (size_t)(rph + RP * (m0 + u)) * D * ES, cg, s[u]);
+    for (int t4 = 0; t4 < TM / 4; ++t4) q[t4] = *(const f32x4 *)(qT + i * TM + 4 * t4);
+  };
+  // One batch of rows.  Every draft is multiplied, with no per-draft branch
+  // (q of drafts t >= T is zero in LDS, and their outputs are not stored).
+  // The next row's q is read while a row is multiplied, and a scheduling
+  // barrier per row keeps the compiler from hoisting all rows' LDS reads
+  // (which would not fit in registers).
+  auto mult_rows = [&](const float(&s)[U][4], int m0) {
+    f32x4 qn[TM / 4];
+    read_q(qn, rph + RP * m0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = rph + RP * (m0 + u);
-      float qv[TM], kv[TM];
+      f32x4 qc[TM / 4];
 #pragma unroll
-      for (int t4 = 0; t4 < TM; t4 += 4) {
-        const f32x4 q4 = *(const f32x4 *)(qT + i * TM + t4);
-        const f32x4 k4 = *(const f32x4 *)(kT + i * TM + t4);
+      for (int t4 = 0; t4 < TM / 4; ++t4) qc[t4] = qn[t4];
+      if (u + 1 < U) read_q(qn, rph + RP * (m0 + u + 1));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qv[t4 + e] = q4[e];
-          kv[t4 + e] = k4[e];
-        }
-      }
-      float c[4];
+      for (int t = 0; t < TM; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] = ST == kStF32 ? s[u][e] : s[u][e] * sc;
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        if (t < T) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            c[e] = fmaf(kv[t], vr[t][e], c[e]);
-            acc[t][e] = fmaf(qv[t], c[e], acc[t][e]);
-          }
-        }
-      }
+        for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(qc[t / 4][t % 4], s[u][e], acc[t][e]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+#pragma unroll 1
+  for (int m0 = 0; m0 < RPL; m0 += U) {
+    float s[U][4];
+    load_rows(s, m0);
+    mult_rows(s, m0);
   }
   // lanes with equal cg hold partial sums over disjoint rows
 #pragma unroll
@@ -208,6 +225,84 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
       if (t < T)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[t][e] += __shfl_xor(acc[t][e], off, 64);
+
+  // this lane's 4 columns of every draft's v, needed only from here on (the
+  // state pass runs without them, with fewer registers); their loads are in
+  // flight while the table below is built
+  float vr[TM][4];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    const size_t base = ((size_t)h * T + t) * D + 4 * cg;
+    if (t < T) {
+      if constexpr (IO_BF16) {
+        const u32x2 w = *(const u32x2 *)((const u16 *)a.v + base);
+        vr[t][0] = __uint_as_float(w[0] << 16);
+        vr[t][1] = __uint_as_float(w[0] & 0xffff0000u);
+        vr[t][2] = __uint_as_float(w[1] << 16);
+        vr[t][3] = __uint_as_float(w[1] & 0xffff0000u);
+      } else {
+        const f32x4 w = *(const f32x4 *)((const float *)a.v + base);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[t][e] = w[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vr[t][e] = 0.f;
+    }
+  }
+
+  // P[t][s] = q_t . k_s.  Lane l takes pair group g = l % G (draft t and
+  // drafts s0 .. s0 + 3) over row slice l / G; the slices are summed across
+  // lanes.  Entries with t or s >= T are never read.
+  {
+    constexpr int G = TM * TM / 4, NS = 64 / G, RS = D / NS;
+    static_assert(64 % G == 0 && D % NS == 0, "pair groups");
+    const int g = lane % G, sl = lane / G, tq = g / (TM / 4), s0 = 4 * (g % (TM / 4));
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int i = sl * RS; i < (sl + 1) * RS; ++i) {
+      const float qi = qT[i * TM + tq];
+      f32x4 k4;
+      if constexpr (IO_BF16) {
+        const u32x2 w = *(const u32x2 *)(kT + i * TM + s0);
+        k4 = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                   __uint_as_float(w[1] & 0xffff0000u)};
+      } else {
+        k4 = *(const f32x4 *)(kT + i * TM + s0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = fmaf(qi, k4[e], p[e]);
+    }
+#pragma unroll
+    for (int off = G; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] += __shfl_xor(p[e], off, 64);
+    if (sl == 0) *(f32x4 *)(P + tq * TM + s0) = p;
+  }
+  // the table was written by other lanes of this wave: LDS accesses complete
+  // before it is read
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+
+  // o_t = scale * (q_t^T S) + sum_{s <= t} P[t][s] v_s
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t < T) {
+      float pr[TM];
+#pragma unroll
+      for (int s4 = 0; s4 < TM; s4 += 4) {
+        const f32x4 p4 = *(const f32x4 *)(P + t * TM + s4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[s4 + e] = p4[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][e] = ST == kStF32 ? acc[t][e] : acc[t][e] * sc;
+#pragma unroll
+      for (int s = 0; s <= t; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(pr[s], vr[s][e], acc[t][e]);
+    }
+  }
 
   if (rph == 0) {
 #pragma unroll
@@ -296,13 +391,13 @@ hipError_t go(const DecodeMultiArgs &a, bool commit, hipStream_t stream) {
     const int64_t grid = (a.BH + kWV - 1) / kWV;
     // room for TM = 4, 8 or 16 drafts (registers and LDS scale with it)
     if (a.T <= 4) {
-      const size_t lds = (size_t)kWV * 2 * D * 4 * sizeof(float);
+      const size_t lds = (size_t)kWV * verify_lds_bytes<D, 4, IO>();
       hipLaunchKernelGGL((verify_kernel<D, IO, ST, 4>), dim3((unsigned)grid), dim3(64 * kWV), lds, stream, a);
     } else if (a.T <= 8) {
-      const size_t lds = (size_t)kWV * 2 * D * 8 * sizeof(float);
+      const size_t lds = (size_t)kWV * verify_lds_bytes<D, 8, IO>();
       hipLaunchKernelGGL((verify_kernel<D, IO, ST, 8>), dim3((unsigned)grid), dim3(64 * kWV), lds, stream, a);
     } else {
-      const size_t lds = (size_t)kWV * 2 * D * 16 * sizeof(float);  // 32 KiB at d = 128
+      const size_t lds = (size_t)kWV * verify_lds_bytes<D, 16, IO>();  // 26 KiB at d = 128, bf16 I/O
       hipLaunchKernelGGL((verify_kernel<D, IO, ST, 16>), dim3((unsigned)grid), dim3(64 * kWV), lds, stream, a);
     }
   }
