@@ -321,28 +321,67 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   }
 }
 
-template <int D, bool IO_BF16, int ST>
-__global__ __launch_bounds__(64 * kW) void commit_kernel(DecodeMultiArgs a) {
+// commit, with TM >= T drafts of room: per state element, the accepted
+// drafts' updates in draft order, the fused multiply-adds of as many
+// one-token decode steps.  k of the drafts is staged in LDS (transposed,
+// fp32) with 16-byte loads, each group issued before its stores; each lane keeps its
+// 4 columns of the accepted drafts' v in registers.  The pass is bound by
+// the state bytes in flight, so each variant asks the compiler for the
+// occupancy its registers allow without spills (8, 6 and 3 waves per SIMD
+// with room for 4, 8 and 16 drafts).
+constexpr int commit_waves_per_simd(int TM) { return TM <= 4 ? 8 : TM <= 8 ? 6 : 3; }
+
+template <int D, bool IO_BF16, int ST, int TM>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(commit_waves_per_simd(TM))))
+void commit_kernel(DecodeMultiArgs a) {
   constexpr int ES = ST == kStF32 ? 4 : ST == kStBF16 ? 2 : 1;
   constexpr int LPR = D / 4;
   constexpr int RP = 64 / LPR;
   constexpr int RPL = D / RP;
   constexpr int U = 8;
   static_assert(RPL % U == 0, "row unroll");
+  static_assert(TM % 4 == 0, "LDS rows of whole float4s");
+  constexpr int EPC = IO_BF16 ? 8 : 4;          // elements per 16-byte piece of k
+  constexpr int NP = (D * TM / EPC + 63) / 64;  // pieces per lane, at most
   extern __shared__ float lds[];
   const int T = a.T;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  float *kT = lds + (size_t)wave * D * T;  // kT[i * T + t]
+  float *kT = lds + (size_t)wave * D * TM;  // kT[i * TM + t]
   const int64_t h = (int64_t)blockIdx.x * kW + wave;
   const bool valid = h < a.BH;
   int cnt = 0;
   if (valid) {
     cnt = a.accept ? a.accept[h / a.H] : T;
     cnt = cnt < 0 ? 0 : (cnt > T ? T : cnt);
-    for (int x = lane; x < D * T; x += 64) {
-      const int t = x / D, i = x % D;
-      kT[i * T + t] = ld_io<IO_BF16>(a.k, ((size_t)h * T + t) * D + i);
+    const int npieces = D * T / EPC;
+    const char *kb = (const char *)a.k + (size_t)h * T * D * (IO_BF16 ? 2 : 4);
+    constexpr int NG = NP < 4 ? NP : 4;  // pieces per group
+    static_assert(NP % NG == 0, "piece groups");
+#pragma unroll
+    for (int j0 = 0; j0 < NP; j0 += NG) {
+      u32x4 kp[NG];
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const int c = lane + 64 * (j0 + j);
+        if (c < npieces) kp[j] = *(const u32x4 *)(kb + (size_t)c * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const int c = lane + 64 * (j0 + j);
+        if (c < npieces) {
+          const int t = c * EPC / D, i0 = c * EPC % D;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            if constexpr (IO_BF16) {
+              const uint32_t w = kp[j][e / 2];
+              kT[(i0 + e) * TM + t] = __uint_as_float(e & 1 ? w & 0xffff0000u : w << 16);
+            } else {
+              kT[(i0 + e) * TM + t] = __uint_as_float(kp[j][e]);
+            }
+          }
+        }
+      }
     }
   }
   __syncthreads();
@@ -352,12 +391,27 @@ __global__ __launch_bounds__(64 * kW) void commit_kernel(DecodeMultiArgs a) {
   const int cg = lane % LPR, rph = lane / LPR;
   // narrow states are updated in stored units: v / scale
   const float inv = (ST != kStF32 && a.scale) ? 1.f / a.scale[h] : 1.f;
-  float vr[kTMax][4];
+  float vr[TM][4];
 #pragma unroll
-  for (int t = 0; t < kTMax; ++t)
+  for (int t = 0; t < TM; ++t) {
+    const size_t base = ((size_t)h * T + t) * D + 4 * cg;
+    float w[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < cnt) {
+      if constexpr (IO_BF16) {
+        const u32x2 x = *(const u32x2 *)((const u16 *)a.v + base);
+        w[0] = __uint_as_float(x[0] << 16);
+        w[1] = __uint_as_float(x[0] & 0xffff0000u);
+        w[2] = __uint_as_float(x[1] << 16);
+        w[3] = __uint_as_float(x[1] & 0xffff0000u);
+      } else {
+        const f32x4 x = *(const f32x4 *)((const float *)a.v + base);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      vr[t][e] = t < cnt ? ld_io<IO_BF16>(a.v, ((size_t)h * T + t) * D + 4 * cg + e) * inv : 0.f;
+        for (int e = 0; e < 4; ++e) w[e] = x[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vr[t][e] = w[e] * inv;
+  }
 
   char *Sh = (char *)a.state + (size_t)h * D * D * ES;
   for (int m0 = 0; m0 < RPL; m0 += U) {
@@ -367,13 +421,14 @@ __global__ __launch_bounds__(64 * kW) void commit_kernel(DecodeMultiArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = rph + RP * (m0 + u);
-      const float *ki = kT + i * T;
+      f32x4 k4[TM / 4];
 #pragma unroll
-      for (int t = 0; t < kTMax; ++t) {
+      for (int t4 = 0; t4 < TM / 4; ++t4) k4[t4] = *(const f32x4 *)(kT + i * TM + 4 * t4);
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
         if (t < cnt) {
-          const float kv = ki[t];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[u][e] = fmaf(kv, vr[t][e], s[u][e]);
+          for (int e = 0; e < 4; ++e) s[u][e] = fmaf(k4[t / 4][t % 4], vr[t][e], s[u][e]);
         }
       }
       st_state4<ST>(Sh + (size_t)i * D * ES, cg, s[u]);
@@ -385,8 +440,16 @@ template <int D, bool IO, int ST>
 hipError_t go(const DecodeMultiArgs &a, bool commit, hipStream_t stream) {
   if (commit) {
     const int64_t grid = (a.BH + kW - 1) / kW;
-    const size_t lds = (size_t)kW * D * a.T * sizeof(float);  // <= 32 KiB
-    hipLaunchKernelGGL((commit_kernel<D, IO, ST>), dim3((unsigned)grid), dim3(64 * kW), lds, stream, a);
+    // room for TM = 4, 8 or 16 drafts; LDS kW * D * TM floats, <= 32 KiB
+    if (a.T <= 4)
+      hipLaunchKernelGGL((commit_kernel<D, IO, ST, 4>), dim3((unsigned)grid), dim3(64 * kW),
+                         (size_t)kW * D * 4 * sizeof(float), stream, a);
+    else if (a.T <= 8)
+      hipLaunchKernelGGL((commit_kernel<D, IO, ST, 8>), dim3((unsigned)grid), dim3(64 * kW),
+                         (size_t)kW * D * 8 * sizeof(float), stream, a);
+    else
+      hipLaunchKernelGGL((commit_kernel<D, IO, ST, 16>), dim3((unsigned)grid), dim3(64 * kW),
+                         (size_t)kW * D * 16 * sizeof(float), stream, a);
   } else {
     const int64_t grid = (a.BH + kWV - 1) / kWV;
     // room for TM = 4, 8 or 16 drafts (registers and LDS scale with it)
