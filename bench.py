@@ -341,6 +341,8 @@ def hbm_ceiling(torch, reps: int = 5):
                 if i >= 2:
                     ms.append(e0.elapsed_time(e1))
             gbs = moved / (sum(ms) / len(ms) / 1e3) / 1e9
+            if gbs > 1.05 * PEAK_HBM_GBS:  # the probe skipped work it was asked to do
+                raise RuntimeError(f"hbm_stream {name} batch={batch} measured {gbs:.0f} GB/s, above the HBM peak")
             if best is None or gbs > best[0]:
                 best = (gbs, nt, wgs, batch)
         out[name + "_GBps"] = best[0]
