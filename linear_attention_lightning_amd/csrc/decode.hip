@@ -79,33 +79,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void decode_kernel(DecodeArgs 
   u32x4 *Sh = (u32x4 *)((char *)a.state + (size_t)h * D * D * ES);  // 16-byte units
   constexpr int U16_PER_ROW = D * ES / 16;
 
-  for (int m0 = 0; m0 < RPL; m0 += U) {
-    u32x4 raw[U];
+  if constexpr (ST == kStE4M3) {
+    // one batch of U rows per lane, the loop kept rolled: this form measured
+    // 5 % faster than the loop over both batches written out
+    auto rows = [&](int m0) {
+      u32x4 raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = rph + RP * (m0 + u);
-      raw[u] = __builtin_nontemporal_load(Sh + (size_t)i * U16_PER_ROW + cg);
-    }
+      for (int u = 0; u < U; ++u) {
+        const int i = rph + RP * (m0 + u);
+        raw[u] = __builtin_nontemporal_load(Sh + (size_t)i * U16_PER_ROW + cg);
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = rph + RP * (m0 + u);
-      const float2 qki = qk[wave][i];
-      u32x4 w;
-      if constexpr (ST == kStBF16) {
-        // each 32-bit word holds two bf16 state entries (low half first)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const uint32_t word = raw[u][x];
-          float s0 = __uint_as_float(word << 16);
-          float s1 = __uint_as_float(word & 0xffff0000u);
-          s0 = fmaf(qki.y, vj[2 * x], s0);
-          s1 = fmaf(qki.y, vj[2 * x + 1], s1);
-          acc[2 * x] = fmaf(qki.x, s0, acc[2 * x]);
-          acc[2 * x + 1] = fmaf(qki.x, s1, acc[2 * x + 1]);
-          const bf16x2 packed = {(bf16)s0, (bf16)s1};
-          w[x] = __builtin_bit_cast(uint32_t, packed);
-        }
-      } else if constexpr (ST == kStE4M3) {
+      for (int u = 0; u < U; ++u) {
+        const int i = rph + RP * (m0 + u);
+        const float2 qki = qk[wave][i];
+        u32x4 w;
         // each 32-bit word holds four fp8 state entries (byte 0 first)
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -117,15 +105,48 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void decode_kernel(DecodeArgs 
           }
           w[x] = f32_to_e4m3x4(sv);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float se = fmaf(qki.y, vj[e], __uint_as_float(raw[u][e]));
-          acc[e] = fmaf(qki.x, se, acc[e]);
-          w[e] = __float_as_uint(se);
-        }
+        __builtin_nontemporal_store(w, Sh + (size_t)i * U16_PER_ROW + cg);
       }
-      __builtin_nontemporal_store(w, Sh + (size_t)i * U16_PER_ROW + cg);
+    };
+#pragma unroll 1
+    for (int m0 = 0; m0 < RPL; m0 += U) rows(m0);
+  } else {
+    for (int m0 = 0; m0 < RPL; m0 += U) {
+      u32x4 raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = rph + RP * (m0 + u);
+        raw[u] = __builtin_nontemporal_load(Sh + (size_t)i * U16_PER_ROW + cg);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = rph + RP * (m0 + u);
+        const float2 qki = qk[wave][i];
+        u32x4 w;
+        if constexpr (ST == kStBF16) {
+          // each 32-bit word holds two bf16 state entries (low half first)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const uint32_t word = raw[u][x];
+            float s0 = __uint_as_float(word << 16);
+            float s1 = __uint_as_float(word & 0xffff0000u);
+            s0 = fmaf(qki.y, vj[2 * x], s0);
+            s1 = fmaf(qki.y, vj[2 * x + 1], s1);
+            acc[2 * x] = fmaf(qki.x, s0, acc[2 * x]);
+            acc[2 * x + 1] = fmaf(qki.x, s1, acc[2 * x + 1]);
+            const bf16x2 packed = {(bf16)s0, (bf16)s1};
+            w[x] = __builtin_bit_cast(uint32_t, packed);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float se = fmaf(qki.y, vj[e], __uint_as_float(raw[u][e]));
+            acc[e] = fmaf(qki.x, se, acc[e]);
+            w[e] = __float_as_uint(se);
+          }
+        }
+        __builtin_nontemporal_store(w, Sh + (size_t)i * U16_PER_ROW + cg);
+      }
     }
   }
 
