@@ -11,7 +11,9 @@
 // entries of one column in registers.  Tokens are processed in batches of 32:
 // q, k and the v slice of a batch are staged in LDS, each thread runs the
 // recurrence over the batch and leaves its partial o_t (a sum over its rows)
-// in LDS, and the partials are then reduced and stored.
+// in LDS, and the partials are then reduced and stored.  The next batch's q,
+// k and v are loaded (16-byte pieces) into registers while a batch is
+// computed, so only the first batch waits for memory.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -52,22 +54,55 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
 #pragma unroll
   for (int m = 0; m < RPT; ++m) S[m] = Sh[(size_t)(rg + kGroups * m) * D + j0 + jj];
 
+  // a batch's q, k and v slice in 16-byte pieces of EPC elements: QP pieces of
+  // q and of k per thread, and one v piece for the first VP threads.  Pieces
+  // of tokens at or past N are zero.
+  constexpr int EPC = IO_BF16 ? 8 : 4;
+  constexpr int QP = kTB * D / EPC / kThreads;
+  constexpr int VP = kTB * kCols / EPC;
+  static_assert(QP * EPC * kThreads == kTB * D && VP <= kThreads && kCols % EPC == 0, "batch pieces");
+  constexpr int ES = IO_BF16 ? 2 : 4;
+  u32x4 qp[QP], kp[QP], vp;
+  auto load_batch = [&](int64_t tok0) {
+#pragma unroll
+    for (int j = 0; j < QP; ++j) {
+      const int c = tid + kThreads * j, tt = c * EPC / D, i0 = c * EPC % D;
+      qp[j] = kp[j] = u32x4{0u, 0u, 0u, 0u};
+      if (tok0 + tt < N) {
+        const size_t off = (base + (size_t)(tok0 + tt) * D + i0) * ES;
+        qp[j] = *(const u32x4 *)((const char *)a.q + off);
+        kp[j] = *(const u32x4 *)((const char *)a.k + off);
+      }
+    }
+    vp = u32x4{0u, 0u, 0u, 0u};
+    if (tid < VP) {
+      const int tt = tid * EPC / kCols, c0 = tid * EPC % kCols;
+      if (tok0 + tt < N) vp = *(const u32x4 *)((const char *)a.v + (base + (size_t)(tok0 + tt) * D + j0 + c0) * ES);
+    }
+  };
+  auto elem = [&](const u32x4 &p, int e) -> float {
+    if constexpr (IO_BF16)
+      return __uint_as_float(e & 1 ? p[e / 2] & 0xffff0000u : p[e / 2] << 16);
+    else
+      return __uint_as_float(p[e]);
+  };
+
+  load_batch(0);
   for (int64_t tok0 = 0; tok0 < N; tok0 += kTB) {
     const int n = (int)((N - tok0) < kTB ? (N - tok0) : kTB);
-    for (int idx = tid; idx < kTB * D; idx += kThreads) {
-      const int tt = idx / D, i = idx % D;
-      float2 x = make_float2(0.f, 0.f);
-      if (tt < n) {
-        const size_t off = base + (size_t)(tok0 + tt) * D + i;
-        x = make_float2(ld<IO_BF16>(a.q, off), ld<IO_BF16>(a.k, off));
-      }
-      qk[tt][i] = x;
+#pragma unroll
+    for (int j = 0; j < QP; ++j) {
+      const int c = tid + kThreads * j, tt = c * EPC / D, i0 = c * EPC % D;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) qk[tt][i0 + e] = make_float2(elem(qp[j], e), elem(kp[j], e));
     }
-    for (int idx = tid; idx < kTB * kCols; idx += kThreads) {
-      const int tt = idx / kCols, c = idx % kCols;
-      vv[tt][c] = (tt < n) ? ld<IO_BF16>(a.v, base + (size_t)(tok0 + tt) * D + j0 + c) : 0.f;
+    if (tid < VP) {
+      const int tt = tid * EPC / kCols, c0 = tid * EPC % kCols;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) vv[tt][c0 + e] = elem(vp, e);
     }
     __syncthreads();
+    if (tok0 + kTB < N) load_batch(tok0 + kTB);  // in flight during this batch
     for (int tt = 0; tt < n; ++tt) {
       const float vj = vv[tt][jj];
       float part = 0.f;
