@@ -7,8 +7,9 @@
 // that the tiled kernel is measured against.
 //
 // Value columns of the state are independent, so a workgroup owns one
-// (sequence, 16-column slice): each of its 256 threads keeps d/16 fp32 state
-// entries of one column in registers.  Tokens are processed in batches of 32:
+// (sequence, 8-column slice): each of its 256 threads keeps d/32 fp32 state
+// entries of one column in registers.  Narrow slices give few sequences
+// enough workgroups (8 heads of d = 128: 128 workgroups).  Tokens are processed in batches of 32:
 // q, k and the v slice of a batch are staged in LDS, each thread runs the
 // recurrence over the batch and leaves its partial o_t (a sum over its rows)
 // in LDS, and the partials are then reduced and stored.  The next batch's q,
@@ -21,8 +22,8 @@ namespace lal {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCols = 16;    // value columns per workgroup
-constexpr int kGroups = 16;  // row groups (threads per column)
+constexpr int kCols = 8;     // value columns per workgroup
+constexpr int kGroups = 32;  // row groups (threads per column)
 constexpr int kTB = 32;      // tokens per batch
 
 template <bool BF16>
