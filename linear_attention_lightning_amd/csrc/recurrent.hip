@@ -7,9 +7,12 @@
 // that the tiled kernel is measured against.
 //
 // Value columns of the state are independent, so a workgroup owns one
-// (sequence, 8-column slice): each of its 256 threads keeps d/32 fp32 state
-// entries of one column in registers.  Narrow slices give few sequences
-// enough workgroups (8 heads of d = 128: 128 workgroups).  Tokens are processed in batches of 32:
+// (sequence, COLS-column slice): each of its 256 threads keeps COLS * d / 256
+// fp32 state entries of one column in registers.  16-column slices are used
+// when they give every compute unit a workgroup; fewer sequences get 8-column
+// slices and twice the workgroups (8 heads of d = 128: 128 instead of 64).
+// Each workgroup stages whole q and k rows, so narrower slices cost more
+// staging and are slower once the GPU is full.  Tokens are processed in batches of 32:
 // q, k and the v slice of a batch are staged in LDS, each thread runs the
 // recurrence over the batch and leaves its partial o_t (a sum over its rows)
 // in LDS, and the partials are then reduced and stored.  The next batch's q,
@@ -22,21 +25,13 @@ namespace lal {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCols = 8;     // value columns per workgroup
-constexpr int kGroups = 32;  // row groups (threads per column)
 constexpr int kTB = 32;      // tokens per batch
 
-template <bool BF16>
-__device__ __forceinline__ float ld(const void *p, size_t i) {
-  if constexpr (BF16)
-    return bf16_bits_to_f32(((const u16 *)p)[i]);
-  else
-    return ((const float *)p)[i];
-}
-
-template <int D, bool IO_BF16>
+template <int D, bool IO_BF16, int COLS>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
-  constexpr int RPT = D / kGroups;  // state rows per thread
+  constexpr int kCols = COLS;                 // value columns per workgroup
+  constexpr int kGroups = kThreads / kCols;   // row groups (threads per column)
+  constexpr int RPT = D / kGroups;            // state rows per thread
   __shared__ float2 qk[kTB][D];
   __shared__ float vv[kTB][kCols];
   __shared__ float red[kTB][kGroups][kCols + 1];
@@ -133,10 +128,14 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
   for (int m = 0; m < RPT; ++m) Sh[(size_t)(rg + kGroups * m) * D + j0 + jj] = S[m];
 }
 
+constexpr int kCUs = 256;  // compute units of the target GPU
+
 template <int D, bool IO>
 hipError_t go(const RecurrentArgs &a, hipStream_t stream) {
-  const int64_t grid = a.BH * (D / kCols);
-  hipLaunchKernelGGL((recurrent_kernel<D, IO>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  if (a.BH * (D / 16) >= kCUs)
+    hipLaunchKernelGGL((recurrent_kernel<D, IO, 16>), dim3((unsigned)(a.BH * (D / 16))), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<D, IO, 8>), dim3((unsigned)(a.BH * (D / 8))), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -106,7 +106,9 @@ def test_decode_after_prefill():
 
 
 @pytest.mark.parametrize("B,H,N,d,io", [(1, 2, 300, 128, "bf16"), (2, 1, 77, 64, "bf16"),
-                                        (1, 2, 130, 128, "fp32"), (1, 1, 1, 64, "fp32")])
+                                        (1, 2, 130, 128, "fp32"), (1, 1, 1, 64, "fp32"),
+                                        # enough sequences for the 16-column slices (B*H*d/16 >= 256)
+                                        (2, 16, 200, 128, "bf16"), (4, 16, 45, 64, "fp32")])
 def test_recurrent_prefill(B, H, N, d, io):
     announce("recurrent prefill", B, H, N, d, io)
     q, k, v = synth.prefill_inputs(21, B, H, N, d, io)
