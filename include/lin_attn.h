@@ -37,7 +37,11 @@
  *    thrown across the ABI.  A call with zero work (B*H*N == 0) returns
  *    LIN_ATTN_OK and leaves every buffer untouched.
  *  - The library is reentrant; concurrent calls on different streams are
- *    independent as long as their buffers do not overlap.
+ *    independent as long as their buffers do not overlap.  The only state it
+ *    keeps between calls is a per-device cache of a value that never changes
+ *    while the process runs: the device's compute-unit count (queried once,
+ *    used to size grids and split plans), written with atomic stores, so
+ *    concurrent first calls only repeat the query.
  */
 #ifndef LIN_ATTN_H
 #define LIN_ATTN_H
@@ -303,9 +307,11 @@ int lin_attn_state_accumulate(const void *k, const void *v, float *state,
  * other than the first go to a caller-provided workspace.
  *
  * lin_attn_state_accumulate_split_workspace returns the workspace bytes the
- * call needs for these sizes (0 when a single chunk per sequence suffices,
+ * call needs for these sizes on the current device (the chunk count depends
+ * on its compute-unit count; 0 when a single chunk per sequence suffices,
  * and for fp32 I/O, which runs the unsplit kernel), or a negative error code
- * (LIN_ATTN_EINVAL, LIN_ATTN_EUNSUPPORTED) for arguments the call rejects.
+ * (LIN_ATTN_EINVAL, LIN_ATTN_EUNSUPPORTED) for arguments the call rejects, or
+ * LIN_ATTN_EHIP when the device cannot be queried.
  *
  * workspace       : device pointer, 16-byte aligned, at least that many
  *                   bytes, owned by the caller, not aliasing k, v or state;
@@ -326,9 +332,9 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state,
  * Prefill cut along the tokens, for few sequences: the same outputs and
  * final state as lin_attn_prefill (up to fp32 rounding of the carried
  * state), computed as follows.  Each sequence's N tokens are cut into P equal
- * parts so that B*H*P is at most 256 (one chunked-prefill workgroup per compute
- * unit, before any value-column split; parts of at least 512 tokens, P a power
- * of two dividing N).  The
+ * parts so that B*H*P is at most the device's compute-unit count (one
+ * chunked-prefill workgroup per compute unit, before any value-column split;
+ * parts of at least 512 tokens, P a power of two dividing N).  The
  * K^T V of the first P-1 parts is summed by the token-split accumulation
  * (into the workspace); each part's initial state is S_0 plus the sums of the
  * parts before it, added in part order (the associativity equation of
@@ -341,9 +347,10 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state,
  * call is lin_attn_prefill and needs no workspace.
  *
  * lin_attn_prefill_seqsplit_workspace returns the workspace bytes the call
- * needs, (2P - 1 + (P-1)(S-1)) * B*H * d*d * 4 for S <= 4 accumulation chunks
- * per part (0 when P = 1), or a negative error code for arguments the call
- * rejects.
+ * needs on the current device (the plan depends on its compute-unit count),
+ * (2P - 1 + (P-1)(S-1)) * B*H * d*d * 4 for S <= 4 accumulation chunks per
+ * part (0 when P = 1), or a negative error code for arguments the call
+ * rejects (LIN_ATTN_EHIP when the device cannot be queried).
  * workspace, workspace_bytes: as lin_attn_state_accumulate_split.  Other
  * arguments, layouts and errors as lin_attn_prefill.
  */

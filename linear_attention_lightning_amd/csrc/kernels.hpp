@@ -102,7 +102,8 @@ struct RecurrentArgs {
   int64_t BH;
   int64_t N;
 };
-hipError_t recurrent_launch(RecurrentArgs a, int d, bool io_bf16, hipStream_t stream);
+// cus: compute units of the device (the slice width is chosen to fill them)
+hipError_t recurrent_launch(RecurrentArgs a, int d, bool io_bf16, int cus, hipStream_t stream);
 
 // Several decode tokens per sequence: verify (outputs, state read only) and
 // commit (state += sum over the accepted drafts of k v^T).
@@ -150,7 +151,8 @@ struct StateSplitArgs {
 };
 hipError_t state_split_launch(StateSplitArgs a, int d, hipStream_t stream);
 // chunks and chunk length (a multiple of 64) for BH sequences of N >= 1 tokens
-void state_split_plan(int64_t BH, int64_t N, int64_t *chunks, int64_t *chunk_len);
+// on a device of `cus` compute units
+void state_split_plan(int64_t BH, int64_t N, int cus, int64_t *chunks, int64_t *chunk_len);
 
 // Initial states of the P parts of each sequence for a prefill cut along the
 // tokens: starts[bh P + p] = state[bh] + sum over chunks c < p S of

@@ -311,8 +311,11 @@ int lin_attn_prefill_recurrent(const void *q, const void *k, const void *v, void
   if (BH == 0 || N == 0) return LIN_ATTN_OK;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
   if (BH * (d / 16) > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  int cus = 0;
+  const int rc = cu_count(&cus);
+  if (rc != LIN_ATTN_OK) return rc;
   lal::RecurrentArgs a{q, k, v, o, state, BH, N};
-  return from_hip(lal::recurrent_launch(a, (int)d, io_dtype == LIN_ATTN_BF16, (hipStream_t)stream));
+  return from_hip(lal::recurrent_launch(a, (int)d, io_dtype == LIN_ATTN_BF16, cus, (hipStream_t)stream));
 }
 
 namespace {
@@ -406,7 +409,10 @@ int split_check(int64_t B, int64_t H, int64_t N, int64_t d, lin_attn_dtype_t io_
   *chunk_len = N;
   *ws_bytes = 0;
   if (BH == 0 || N == 0 || io_dtype == LIN_ATTN_F32) return LIN_ATTN_OK;
-  lal::state_split_plan(BH, N, chunks, chunk_len);
+  int cus = 0;
+  const int rc = cu_count(&cus);
+  if (rc != LIN_ATTN_OK) return rc;
+  lal::state_split_plan(BH, N, cus, chunks, chunk_len);
   int64_t groups;
   if (!mul_ok(BH, *chunks, &groups) || groups > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
   if (!mul_ok((*chunks - 1) * BH, d * d * 4, ws_bytes)) return LIN_ATTN_EINVAL;
@@ -440,11 +446,11 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state, 
 
 namespace {
 
-// Prefill cut along the tokens: P parts per sequence (B*H*P at most 256, parts
-// of at least 512 tokens, P a power of two dividing N); the K^T V of the first
-// P-1 parts is summed in chunks of L/S tokens (S a power of two <= 4 dividing
-// L, chunks of at least 1024 tokens).  Workspace: (P-1) S BH partial states,
-// then BH P part states.
+// Prefill cut along the tokens: P parts per sequence (B*H*P at most the
+// device's compute units, parts of at least 512 tokens, P a power of two
+// dividing N); the K^T V of the first P-1 parts is summed in chunks of L/S
+// tokens (S a power of two <= 4 dividing L, chunks of at least 1024 tokens).
+// Workspace: (P-1) S BH partial states, then BH P part states.
 struct SeqSplitPlan {
   int64_t BH, P, L, S, ws_bytes;
 };
@@ -464,7 +470,10 @@ int seqsplit_check(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, li
   pl->S = 1;
   pl->ws_bytes = 0;
   if (io_dtype == LIN_ATTN_BF16 && BH > 0 && N > 0) {
-    while (BH * pl->P * 2 <= 256 && N % (pl->P * 2) == 0 && N / (pl->P * 2) >= 512) pl->P *= 2;
+    int cus = 0;
+    const int rc = cu_count(&cus);
+    if (rc != LIN_ATTN_OK) return rc;
+    while (BH * pl->P * 2 <= cus && N % (pl->P * 2) == 0 && N / (pl->P * 2) >= 512) pl->P *= 2;
   }
   pl->L = pl->P > 0 ? N / pl->P : N;
   if (pl->P > 1) {
@@ -484,16 +493,15 @@ int64_t lin_attn_prefill_seqsplit_workspace(int64_t B, int64_t H, int64_t N, int
   return rc == LIN_ATTN_OK ? pl.ws_bytes : rc;
 }
 
-int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void *o, float *state, int64_t B,
-                              int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
-                              void *workspace, int64_t workspace_bytes, void *stream) {
-  SeqSplitPlan pl;
-  int rc = seqsplit_check(B, H, N, d, block, io_dtype, &pl);
-  if (rc != LIN_ATTN_OK) return rc;
-  if (workspace_bytes < pl.ws_bytes) return LIN_ATTN_EINVAL;
-  if (pl.P == 1) return prefill_impl(q, k, v, o, state, nullptr, 0, B, H, N, d, block, io_dtype, 0, stream);
-  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state) || !ok_ptr(workspace))
-    return LIN_ATTN_EINVAL;
+namespace {
+
+// The launches of a prefill cut along the tokens (plan pl, P > 1), with the
+// workspace at `workspace` (pl.ws_bytes bytes; every byte the kernels read is
+// written by an earlier launch of the same call, so its contents on entry do
+// not matter).
+int seqsplit_run(const SeqSplitPlan &pl, const void *q, const void *k, const void *v, void *o, float *state,
+                 int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype, void *workspace, void *stream) {
+  int rc;
   hipStream_t s = (hipStream_t)stream;
   float *partial = (float *)workspace;
   float *starts = partial + (size_t)(pl.P - 1) * pl.S * pl.BH * d * d;
@@ -510,6 +518,21 @@ int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void 
   if (rc != LIN_ATTN_OK) return rc;
   // 4. the final state is the last part's
   return from_hip(lal::state_take_last_launch(starts, state, pl.BH, pl.P, (int)d, s));
+}
+
+}  // namespace
+
+int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void *o, float *state, int64_t B,
+                              int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
+                              void *workspace, int64_t workspace_bytes, void *stream) {
+  SeqSplitPlan pl;
+  int rc = seqsplit_check(B, H, N, d, block, io_dtype, &pl);
+  if (rc != LIN_ATTN_OK) return rc;
+  if (workspace_bytes < pl.ws_bytes) return LIN_ATTN_EINVAL;
+  if (pl.P == 1) return prefill_impl(q, k, v, o, state, nullptr, 0, B, H, N, d, block, io_dtype, 0, stream);
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state) || !ok_ptr(workspace))
+    return LIN_ATTN_EINVAL;
+  return seqsplit_run(pl, q, k, v, o, state, N, d, block, io_dtype, workspace, stream);
 }
 
 const char *lin_attn_strerror(int code) {

@@ -128,11 +128,11 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
   for (int m = 0; m < RPT; ++m) Sh[(size_t)(rg + kGroups * m) * D + j0 + jj] = S[m];
 }
 
-constexpr int kCUs = 256;  // compute units of the target GPU
-
+// 16-column slices when they alone give every compute unit a workgroup,
+// else 8-column slices (twice the workgroups)
 template <int D, bool IO>
-hipError_t go(const RecurrentArgs &a, hipStream_t stream) {
-  if (a.BH * (D / 16) >= kCUs)
+hipError_t go(const RecurrentArgs &a, int cus, hipStream_t stream) {
+  if (a.BH * (D / 16) >= cus)
     hipLaunchKernelGGL((recurrent_kernel<D, IO, 16>), dim3((unsigned)(a.BH * (D / 16))), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((recurrent_kernel<D, IO, 8>), dim3((unsigned)(a.BH * (D / 8))), dim3(kThreads), 0, stream, a);
@@ -141,9 +141,9 @@ hipError_t go(const RecurrentArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t recurrent_launch(RecurrentArgs a, int d, bool io_bf16, hipStream_t stream) {
-  if (d == 128) return io_bf16 ? go<128, true>(a, stream) : go<128, false>(a, stream);
-  if (d == 64) return io_bf16 ? go<64, true>(a, stream) : go<64, false>(a, stream);
+hipError_t recurrent_launch(RecurrentArgs a, int d, bool io_bf16, int cus, hipStream_t stream) {
+  if (d == 128) return io_bf16 ? go<128, true>(a, cus, stream) : go<128, false>(a, cus, stream);
+  if (d == 64) return io_bf16 ? go<64, true>(a, cus, stream) : go<64, false>(a, cus, stream);
   return hipErrorInvalidValue;
 }
 

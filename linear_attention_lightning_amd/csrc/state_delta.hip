@@ -466,11 +466,10 @@ hipError_t state_take_last_launch(const float *starts, float *state, int64_t BH,
   return hipGetLastError();
 }
 
-void state_split_plan(int64_t BH, int64_t N, int64_t *chunks, int64_t *chunk_len) {
-  // about one workgroup per compute unit (256 on MI355X; the kernel's
-  // 128 KiB of LDS at d = 128 allows one per unit), and chunks of at least
-  // 256 tokens
-  int64_t C = BH >= 256 ? 1 : 256 / BH;
+void state_split_plan(int64_t BH, int64_t N, int cus, int64_t *chunks, int64_t *chunk_len) {
+  // about one workgroup per compute unit (the kernel's 128 KiB of LDS at
+  // d = 128 allows one per unit), and chunks of at least 256 tokens
+  int64_t C = BH >= cus ? 1 : cus / BH;
   const int64_t cap = N / 256 > 1 ? N / 256 : 1;
   if (C > cap) C = cap;
   int64_t L = (N + C - 1) / C;

@@ -3,7 +3,11 @@
 The library must load, export every function that include/lin_attn.h
 declares, and reject bad arguments on the host before any HIP call (so these
 calls are safe on a machine without a device).  No call here passes
-validation with work to do, so no kernel is ever launched.
+validation with work to do, so no kernel is ever launched.  The module runs
+only in a child process that sees no device (HIP_VISIBLE_DEVICES=-1, started
+by test_abi_no_device.py): should a check ever pass by mistake, the launch
+then fails with LIN_ATTN_EHIP instead of reaching a GPU with the fake
+pointers these tests pass.
 """
 import ctypes
 import os
@@ -16,6 +20,9 @@ import linear_attention_lightning_amd as la
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "lin_attn.h")
+
+pytestmark = pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES") != "-1",
+                                reason="runs in a child process without a visible device (test_abi_no_device.py)")
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails or returns first
 MISALIGNED = 0x10008
@@ -302,45 +309,38 @@ def test_stream_probe_is_a_separate_library():
 
 def test_split_accumulation_workspace_query_and_validation():
     """The workspace query and the split accumulation reject what the call
-    rejects, before any launch; too small a workspace is EINVAL."""
+    rejects, before any launch; too small a workspace is EINVAL.  A query
+    with work to plan needs the device's compute-unit count: without a
+    device it returns LIN_ATTN_EHIP (the sizes are checked on the GPU)."""
     lib = la.library()
     q = lib.lin_attn_state_accumulate_split_workspace
-    assert q(1, 64, 131072, 128, la.BF16) == 3 * 64 * 128 * 128 * 4  # 4 chunks of 32768 tokens
-    assert q(4, 64, 32768, 128, la.BF16) == 0                         # 256 sequences: one chunk each
-    assert q(1, 2, 255, 128, la.BF16) == 0                            # too short to split
-    assert q(1, 2, 3000, 64, la.F32) == 0
+    assert q(1, 64, 131072, 128, la.BF16) == la.EHIP  # plan needs the device
+    assert q(1, 2, 3000, 64, la.F32) == 0             # fp32 I/O: the unsplit kernel
+    assert q(1, 2, 0, 128, la.BF16) == 0              # nothing to do
     assert q(1, 2, 100, 96, la.BF16) == la.EUNSUPPORTED
     assert q(-1, 2, 100, 64, la.BF16) == la.EINVAL
     assert q(1, 2, 100, 64, 7) == la.EUNSUPPORTED
     f = lib.lin_attn_state_accumulate_split
-    need = q(1, 8, 4096, 128, la.BF16)
-    assert need > 0
-    assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 128, la.BF16, FAKE, need - 1, None) == la.EINVAL
-    assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 128, la.BF16, None, need, None) == la.EINVAL
-    assert f(FAKE, FAKE, MISALIGNED, 1, 8, 4096, 128, la.BF16, FAKE, need, None) == la.EINVAL
-    assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 96, la.BF16, FAKE, need, None) == la.EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 96, la.BF16, FAKE, 1 << 20, None) == la.EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, -8, 4096, 128, la.BF16, FAKE, 1 << 20, None) == la.EINVAL
+    assert f(FAKE, FAKE, FAKE, 1, 8, 4096, 128, la.BF16, FAKE, 1 << 20, None) == la.EHIP  # no device
     assert f(FAKE, FAKE, FAKE, 1, 8, 0, 128, la.BF16, None, 0, None) == la.OK  # nothing to do
 
 
 def test_seqsplit_workspace_query_and_validation():
     lib = la.library()
     q = lib.lin_attn_prefill_seqsplit_workspace
-    # 64 sequences of 131072 tokens: 4 parts of 32768, 4 accumulation chunks each:
-    # 3 * 4 * 64 partial states + 64 * 4 part states, 64 KiB each
-    assert q(1, 64, 131072, 128, 128, la.BF16) == (3 * 4 * 64 + 64 * 4) * 128 * 128 * 4
-    assert q(4, 64, 32768, 128, 128, la.BF16) == 0
-    assert q(1, 8, 4095, 128, 128, la.BF16) == 0       # indivisible / short: no cut
-    assert q(1, 8, 4096, 128, 64, la.F32) == 0         # fp32 I/O: the uncut prefill
+    assert q(1, 64, 131072, 128, 128, la.BF16) == la.EHIP  # plan needs the device
+    assert q(1, 8, 4096, 128, 64, la.F32) == 0          # fp32 I/O: the uncut prefill
+    assert q(1, 8, 0, 128, 128, la.BF16) == 0           # nothing to do
     assert q(1, 8, 4096, 128, 100, la.BF16) == la.EUNSUPPORTED
     assert q(1, 8, 4096, 96, 128, la.BF16) == la.EUNSUPPORTED
     assert q(1, -8, 4096, 128, 128, la.BF16) == la.EINVAL
     f = lib.lin_attn_prefill_seqsplit
-    need = q(1, 8, 8192, 128, 128, la.BF16)
-    assert need > 0
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 128, 128, la.BF16)
-    assert f(*args, FAKE, need - 1, None) == la.EINVAL
-    assert f(*args, None, need, None) == la.EINVAL
-    assert f(FAKE, FAKE, FAKE, MISALIGNED, FAKE, 1, 8, 8192, 128, 128, la.BF16, FAKE, need, None) == la.EINVAL
+    assert f(*args, FAKE, 1 << 30, None) == la.EHIP       # no device to plan on
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 96, 128, la.BF16, FAKE, 1 << 30, None) == la.EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 128, 100, la.BF16, FAKE, 1 << 30, None) == la.EUNSUPPORTED
 
 
 def test_backward_strategy_validation():

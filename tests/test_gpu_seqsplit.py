@@ -132,3 +132,24 @@ def test_seqsplit_shard_workload_sampled():
     eo, es = rel_err(oh, o_ref), rel_err(Sh, S_ref)
     print(f"  heads {heads}: rel err o={eo:.3e} state={es:.3e}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+def test_workspace_queries_on_this_device():
+    """The plans behind the workspace queries use the device's compute-unit
+    count; on a 256-unit MI355X they give these sizes."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip(f"sizes below are for 256 compute units, this device has {cus}")
+    lib = la.library()
+    q = lib.lin_attn_state_accumulate_split_workspace
+    assert q(1, 64, 131072, 128, la.BF16) == 3 * 64 * 128 * 128 * 4  # 4 chunks of 32768 tokens
+    assert q(4, 64, 32768, 128, la.BF16) == 0                         # 256 sequences: one chunk each
+    assert q(1, 2, 255, 128, la.BF16) == 0                            # too short to split
+    p = lib.lin_attn_prefill_seqsplit_workspace
+    # 64 sequences of 131072 tokens: 4 parts of 32768, 4 accumulation chunks each:
+    # 3 * 4 * 64 partial states + 64 * 4 part states, 64 KiB each
+    assert p(1, 64, 131072, 128, 128, la.BF16) == (3 * 4 * 64 + 64 * 4) * 128 * 128 * 4
+    assert p(4, 64, 32768, 128, 128, la.BF16) == 0
+    assert p(1, 8, 4095, 128, 128, la.BF16) == 0       # indivisible: no cut
+    # 8 sequences of 8192 tokens: 16 parts of 512, one chunk each
+    assert p(1, 8, 8192, 128, 128, la.BF16) == (15 * 8 + 8 * 16) * 128 * 128 * 4
