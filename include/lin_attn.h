@@ -38,10 +38,12 @@
  *    LIN_ATTN_OK and leaves every buffer untouched.
  *  - The library is reentrant; concurrent calls on different streams are
  *    independent as long as their buffers do not overlap.  The only state it
- *    keeps between calls is a per-device cache of a value that never changes
+ *    keeps between calls is a per-device cache of values that never change
  *    while the process runs: the device's compute-unit count (queried once,
- *    used to size grids and split plans), written with atomic stores, so
- *    concurrent first calls only repeat the query.
+ *    used to size grids and split plans) and, for
+ *    lin_attn_prefill_seqsplit_noalloc alone, the device address of its fixed
+ *    scratch buffer.  Both are written with atomic stores, so concurrent first
+ *    calls only repeat the query.
  */
 #ifndef LIN_ATTN_H
 #define LIN_ATTN_H
@@ -68,7 +70,9 @@ enum {
   LIN_ATTN_OK = 0,
   LIN_ATTN_EINVAL = -1,       /* null pointer with work to do, negative size, misaligned pointer */
   LIN_ATTN_EUNSUPPORTED = -2, /* valid request outside what the kernels implement (d, block, dtype) */
-  LIN_ATTN_EHIP = -3          /* the HIP runtime reported an error (launch or device query) */
+  LIN_ATTN_EHIP = -3,         /* the HIP runtime reported an error (launch or device query) */
+  LIN_ATTN_ESCRATCH = -4      /* lin_attn_prefill_seqsplit_noalloc: the plan needs more scratch
+                                 memory than the fixed buffer holds (lin_attn_scratch_bytes()) */
 };
 
 /*
@@ -360,6 +364,33 @@ int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void 
                               int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
                               lin_attn_dtype_t io_dtype, void *workspace, int64_t workspace_bytes,
                               void *stream);
+
+/*
+ * lin_attn_prefill_seqsplit for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid hipMalloc.  The same plan, kernels and results as
+ * lin_attn_prefill_seqsplit (bitwise), with the workspace taken from a fixed
+ * buffer inside the library instead of an argument.  The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ * The buffer: lin_attn_scratch_bytes() bytes (64 MiB) of device memory per
+ * device the library runs on, held from the library's load until the process
+ * ends.  Its device address is looked up once per device, on the first call
+ * on that device.  Every call on a device uses that device's one buffer, and
+ * nothing in it needs to start at zero: each byte the kernels read was written
+ * earlier in the same call.  Calls that overlap in time on one device
+ * (different streams, or different host threads) therefore race on the
+ * buffer and give wrong results: serialise them, e.g. on one stream.
+ *
+ * Errors: as lin_attn_prefill_seqsplit, with no workspace arguments, plus
+ * LIN_ATTN_ESCRATCH when the plan for these sizes needs more than
+ * lin_attn_scratch_bytes() of workspace (lin_attn_prefill_seqsplit_workspace
+ * gives the amount); that check runs before any launch.
+ */
+int64_t lin_attn_scratch_bytes(void);
+int lin_attn_prefill_seqsplit_noalloc(const void *q, const void *k, const void *v, void *o, float *state,
+                                      int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                                      lin_attn_dtype_t io_dtype, void *stream);
 
 /*
  * Backward pass (training): the gradients of L = sum_t <o_t, dout_t> +

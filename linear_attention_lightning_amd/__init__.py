@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     BWD_SEPARATE,
     BF16,
     EHIP,
+    ESCRATCH,
     EINVAL,
     EUNSUPPORTED,
     F32,
@@ -28,8 +29,10 @@ from ._binding import (  # noqa: F401
     prefill_recurrent,
     prefill_scaled,
     prefill_seqsplit,
+    prefill_seqsplit_noalloc,
     prefill_seqsplit_workspace,
     prefill_snapshots,
+    scratch_bytes,
     snapshot_count,
     state_accumulate,
     state_accumulate_split,
@@ -37,7 +40,8 @@ from ._binding import (  # noqa: F401
     strerror,
 )
 
-__all__ = ["BWD_AUTO", "BWD_SEPARATE", "BWD_PAIRED", "BWD_FUSED", "prefill", "prefill_scaled", "prefill_seqsplit", "prefill_seqsplit_workspace", "backward", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
+__all__ = ["BWD_AUTO", "BWD_SEPARATE", "BWD_PAIRED", "BWD_FUSED", "prefill", "prefill_scaled", "prefill_seqsplit", "prefill_seqsplit_workspace",
+           "prefill_seqsplit_noalloc", "scratch_bytes", "backward", "decode", "decode_verify", "decode_commit", "prefill_recurrent",
            "prefill_snapshots", "snapshot_count", "state_accumulate", "state_accumulate_split",
            "state_accumulate_split_workspace", "strerror", "library", "LinAttnError",
-           "F32", "BF16", "FP8_E4M3", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "LIB_PATH"]
+           "F32", "BF16", "FP8_E4M3", "OK", "EINVAL", "EUNSUPPORTED", "EHIP", "ESCRATCH", "LIB_PATH"]

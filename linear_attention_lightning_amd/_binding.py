@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_lib", "liblin_attn.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
-OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+OK, EINVAL, EUNSUPPORTED, EHIP, ESCRATCH = 0, -1, -2, -3, -4
 
 _lock = threading.Lock()
 _lib = None
@@ -66,6 +66,10 @@ def library() -> ctypes.CDLL:
             lib.lin_attn_prefill_seqsplit_workspace.restype = i64
             lib.lin_attn_prefill_seqsplit.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, p, i64, p]
             lib.lin_attn_prefill_seqsplit.restype = i32
+            lib.lin_attn_scratch_bytes.argtypes = []
+            lib.lin_attn_scratch_bytes.restype = i64
+            lib.lin_attn_prefill_seqsplit_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
+            lib.lin_attn_prefill_seqsplit_noalloc.restype = i32
             lib.lin_attn_decode_verify_scaled.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
             lib.lin_attn_decode_verify_scaled.restype = i32
             lib.lin_attn_decode_commit_scaled.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, i32, p]
@@ -321,6 +325,31 @@ def prefill_seqsplit(q, k, v, o, state, block: int = 128, workspace=None, *, str
                                              workspace.data_ptr(), workspace.numel(), _stream(stream, q.device))
     if rc != OK:
         raise LinAttnError(rc, "lin_attn_prefill_seqsplit")
+    return o
+
+
+def scratch_bytes() -> int:
+    """Size of the library's fixed per-device scratch buffer (``lin_attn_scratch_bytes``)."""
+    return int(library().lin_attn_scratch_bytes())
+
+
+def prefill_seqsplit_noalloc(q, k, v, o, state, block: int = 128, *, stream=None):
+    """``prefill_seqsplit`` with the workspace taken from the library's fixed
+    per-device scratch buffer (``lin_attn_prefill_seqsplit_noalloc``): no
+    device memory is allocated, here or in the library.  Calls that overlap
+    on one device race on that buffer."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, n, (B, H, N, d), q.dtype, q.device)
+    _check(state, "state", (B, H, d, d), torch.float32, q.device)
+    rc = library().lin_attn_prefill_seqsplit_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                     state.data_ptr(), B, H, N, d, int(block), _dtype_code(q),
+                                                     _stream(stream, q.device))
+    if rc != OK:
+        raise LinAttnError(rc, "lin_attn_prefill_seqsplit_noalloc")
     return o
 
 

@@ -8,6 +8,14 @@
 #include "kernels.hpp"
 #include "lin_attn.h"
 
+// Fixed device memory of lin_attn_prefill_seqsplit_noalloc: one copy per
+// device, held from the library's load until the process ends.  In host code
+// the name is a host-side stand-in, not a device address: the address of each
+// device's copy comes from hipGetSymbolAddress (scratch_ptr below), and only
+// that address is passed to kernels.
+constexpr int64_t kScratchBytes = 64ll << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -39,6 +47,27 @@ int cu_count(int *out) {
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? LIN_ATTN_OK : LIN_ATTN_EHIP; }
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on each device and cached.
+int scratch_ptr(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LIN_ATTN_EHIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    void *p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) {
+      *out = p;
+      return LIN_ATTN_OK;
+    }
+  }
+  void *p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return LIN_ATTN_EHIP;
+  if (dev >= 0 && dev < kMaxDevices) g_scratch_ptr[dev].store(p, std::memory_order_relaxed);
+  *out = p;
+  return LIN_ATTN_OK;
+}
 
 }  // namespace
 
@@ -535,12 +564,32 @@ int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void 
   return seqsplit_run(pl, q, k, v, o, state, N, d, block, io_dtype, workspace, stream);
 }
 
+int64_t lin_attn_scratch_bytes(void) { return kScratchBytes; }
+
+int lin_attn_prefill_seqsplit_noalloc(const void *q, const void *k, const void *v, void *o, float *state,
+                                      int64_t B, int64_t H, int64_t N, int64_t d, int64_t block,
+                                      lin_attn_dtype_t io_dtype, void *stream) {
+  SeqSplitPlan pl;
+  int rc = seqsplit_check(B, H, N, d, block, io_dtype, &pl);
+  if (rc != LIN_ATTN_OK) return rc;
+  if (pl.ws_bytes > kScratchBytes) return LIN_ATTN_ESCRATCH;
+  if (pl.P == 1) return prefill_impl(q, k, v, o, state, nullptr, 0, B, H, N, d, block, io_dtype, 0, stream);
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
+  void *ws = nullptr;
+  rc = scratch_ptr(&ws);
+  if (rc != LIN_ATTN_OK) return rc;
+  return seqsplit_run(pl, q, k, v, o, state, N, d, block, io_dtype, ws, stream);
+}
+
 const char *lin_attn_strerror(int code) {
   switch (code) {
     case LIN_ATTN_OK: return "success";
     case LIN_ATTN_EINVAL: return "invalid argument (null or misaligned pointer, negative or overflowing size)";
     case LIN_ATTN_EUNSUPPORTED: return "unsupported configuration (head dim, block size, split or dtype)";
     case LIN_ATTN_EHIP: return "HIP runtime error";
+    case LIN_ATTN_ESCRATCH:
+      return "the call needs more scratch memory than the library's fixed per-device buffer holds "
+             "(lin_attn_scratch_bytes())";
     default: return "unknown error code";
   }
 }

@@ -67,7 +67,7 @@ def test_library_is_gfx950_only(tmp_path):
 
 def test_strerror():
     assert la.strerror(la.OK) == "success"
-    for c in (la.EINVAL, la.EUNSUPPORTED, la.EHIP):
+    for c in (la.EINVAL, la.EUNSUPPORTED, la.EHIP, la.ESCRATCH):
         assert la.strerror(c) and la.strerror(c) != "success"
     assert "unknown" in la.strerror(12345)
 
@@ -341,6 +341,20 @@ def test_seqsplit_workspace_query_and_validation():
     assert f(*args, FAKE, 1 << 30, None) == la.EHIP       # no device to plan on
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 96, 128, la.BF16, FAKE, 1 << 30, None) == la.EUNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 128, 100, la.BF16, FAKE, 1 << 30, None) == la.EUNSUPPORTED
+
+
+def test_seqsplit_noalloc_validation():
+    """The scratch-buffer variant rejects what the workspace variant rejects,
+    and reports its fixed buffer size; it needs no workspace arguments."""
+    lib = la.library()
+    assert lib.lin_attn_scratch_bytes() == 64 << 20
+    f = lib.lin_attn_prefill_seqsplit_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 96, 128, la.BF16, None) == la.EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 128, 100, la.BF16, None) == la.EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 8192, 128, 128, la.BF16, None) == la.EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 128, 128, 7, None) == la.EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 0, 128, 128, la.BF16, None) == la.OK  # nothing to do
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 128, 128, la.BF16, None) == la.EHIP  # no device
 
 
 def test_backward_strategy_validation():
