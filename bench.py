@@ -28,7 +28,7 @@ sequence split (see long_context).
 launched one by one and replayed from a HIP graph (see decode_steps; the
 default run includes it).
 ``--only ceiling`` measures the HBM bandwidth a plain streaming kernel
-reaches for the path's read:write byte mixes (see hbm_ceiling); the default
+reaches for the path's read:write byte mixes (see hbm_stream_reference); the default
 run includes it.
 ``--only drift`` instead measures the rounding drift of stored states against
 the fp64 oracle along one 1M-token sequence (not part of a step; see
@@ -64,7 +64,8 @@ DRAFTS = 4      # draft tokens verified per sequence in the speculative step
 
 PREFILL_KERNEL_SOURCES = ["linear_attention_lightning_amd/csrc/prefill_bf16_kernel.hpp",
                           "linear_attention_lightning_amd/csrc/prefill_bf16.hip",
-                          "linear_attention_lightning_amd/csrc/common.hpp"]
+                          "linear_attention_lightning_amd/csrc/common.hpp",
+                          "linear_attention_lightning_amd/csrc/kernels.hpp"]
 PROBE_LIB = os.path.join(ROOT, "linear_attention_lightning_amd", "_lib", "libhbm_stream.so")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_B4_H64_N32768_d128_blk128_hbm_traffic.md")
 
@@ -135,44 +136,117 @@ def measured_traffic():
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(heads: int = 64, min_seconds: float = 10.0, max_passes: int = 60):
-    """The fp64 oracle, timed on this host on a bounded sample of the prefill
-    workload: `heads` whole sequences (N = 32768, d = 128; by default the 64
-    heads of one batch entry) with the workload's distributions, recomputed
-    pass after pass until at least `min_seconds` have elapsed.  Reported in
-    the metric's unit: tokens/s, one token being a position of all 64 heads
-    (head-tokens/s divided by 64)."""
-    from linear_attention_lightning_amd import synth
+def _host(t):
+    return t.float().cpu().numpy()
+
+
+def _rel_err(a, b):
+    import numpy as np
+    den = float(np.max(np.abs(b)))
+    return float(np.max(np.abs(np.asarray(a, np.float64) - b)) / den) if den > 0 else float(np.max(np.abs(a)))
+
+
+def cpu_baseline(prefill, small, decode, long_sample, reps: int = 3):
+    """The fp64 oracle, timed on this host's cores on the values the GPU
+    computed on (copied from device memory), and the GPU's outputs of the
+    last timed step compared with it (max|gpu - oracle| / max|oracle|, for the
+    outputs and the final states).  Times are medians of `reps` runs of the
+    compute only (no copies, no generation):
+      * the prefill workload (B=4 H=64 N=32768 d=128): batch entry 0, its 64
+        heads -- the sample; the rate is reported in the metric's unit,
+        tokens/s, one token being a position of all 64 heads;
+      * the crossover workload (B=1 H=8 N=4096 d=128): all of it;
+      * the decode workload (256 x 64 sequences, d=128): one step, all of it;
+      * the long-context workload (B=1 H=64 N=2^20 d=128): the 4 heads of
+        LONG_HEADS, one run; the whole-workload time is extrapolated (x16)
+        and labelled so.
+    prefill, small: (q, k, v, S_in, o, S_out) device tensors of the sampled
+    heads; decode: (q, k, v, S_in, o, S_out) of the whole step; long_sample:
+    from long_context(keep_sample=True), or None."""
+    import numpy as np
     from oracle import oracle
-    N, d, H = PREFILL["N"], PREFILL["d"], PREFILL["H"]
-    q, k, v = synth.prefill_inputs(3, 1, heads, N, d)
     threads = oracle.default_threads()
-    oracle.recurrence(q[:, :1, :256], k[:, :1, :256], v[:, :1, :256])  # load + warm the library
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.recurrence(q, k, v, nthreads=threads)
-        passes += 1
+    oracle.recurrence(np.zeros((1, 8, 16), np.float32), np.zeros((1, 8, 16), np.float32),
+                      np.zeros((1, 8, 16), np.float32))  # load + warm the library
+
+    def timed(fn):
+        ts, out = [], None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            out = fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2], out
+
+    configs, errors = {}, {}
+    # prefill and crossover workloads: the token-by-token fp64 recurrence
+    for name, (tensors, H_all) in (("prefill_B4_H64_N32768", (prefill, 64)),
+                                   ("crossover_B1_H8_N4096", (small, 8))):
+        q, k, v, S_in, o_gpu, S_gpu = tensors
+        qh, kh, vh = _host(q), _host(k), _host(v)
+        S0 = S_in.double().cpu().numpy()
+        dt, (o_ref, S_ref) = timed(lambda: oracle.recurrence(qh, kh, vh, S0, nthreads=threads))
+        heads, N, d = qh.shape[-3], qh.shape[-2], qh.shape[-1]
+        configs[name] = {"seconds_median": dt, "heads": heads, "tokens_per_head": N,
+                         "head_tokens_per_s": heads * N / dt,
+                         "tokens_per_s": heads * N / dt / H_all,
+                         "gflops_fp64": heads * N * 4 * d * d / dt / 1e9}
+        errors[name] = {"o": _rel_err(_host(o_gpu), o_ref), "state": _rel_err(S_gpu.cpu().numpy(), S_ref),
+                        "heads_checked": heads}
+    # decode workload: one step of all 16384 sequences from the state it started from
+    q, k, v, S_in, o_gpu, S_gpu = decode
+    qh, kh, vh = _host(q), _host(k), _host(v)
+    S_start = S_in.double().cpu().numpy()
+    state = {}
+
+    def one_step():
+        S = S_start.copy()
+        o = oracle.decode_step(qh, kh, vh, S, nthreads=threads)
+        state["S"] = S
+        return o
+
+    dt, o_ref = timed(one_step)
+    nseq = qh.shape[0] * qh.shape[1]
+    configs["decode_256x64_d128"] = {"seconds_median": dt, "sequences": nseq, "tokens_per_s": qh.shape[0] / dt,
+                                     "state_GBps_fp64": nseq * 2 * 128 * 128 * 8 / dt / 1e9}
+    errors["decode_256x64_d128"] = {"o": _rel_err(_host(o_gpu), o_ref),
+                                    "state": _rel_err(S_gpu.cpu().numpy(), state["S"])}
+    # long-context workload: 4 heads, one run
+    if long_sample is not None:
+        qh, kh, vh = long_sample["inputs"]
+        t0 = time.perf_counter()
+        o_ref, S_ref = oracle.recurrence(qh, kh, vh, nthreads=threads)
         dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= max_passes:
-            break
-    head_tokens = heads * N * passes
+        N = qh.shape[-2]
+        configs["long_B1_H64_N1048576"] = {
+            "seconds_4_heads": dt, "heads": len(LONG_HEADS), "runs": 1,
+            "extrapolated_seconds_64_heads": dt / -(-len(LONG_HEADS) // threads) * -(-64 // threads),
+            "extrapolation": "extrapolated, not measured: the oracle runs one head per thread, so 64 heads take "
+                             "ceil(64 / threads) rounds of the per-round time of the 4-head run",
+            "head_tokens_per_s": len(LONG_HEADS) * N / dt}
+        for way in ("seqsplit", "value_split"):
+            o_gpu, S_gpu = long_sample[way]
+            errors[f"long_B1_H64_N1048576_{way}"] = {"o": _rel_err(o_gpu, o_ref), "state": _rel_err(S_gpu, S_ref),
+                                                     "heads_checked": list(LONG_HEADS)}
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
             cpu_model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), "")
     except OSError:
         pass
-    return {
-        "value": head_tokens / dt / H,
+    head = configs["prefill_B4_H64_N32768"]
+    baseline = {
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
-        "cores": min(threads, heads),
+        "cores": threads,
         "host_cpus": os.cpu_count(),
         "cpu_model": cpu_model,
         "kind": "oracle",
-        "sample": f"{heads} of the 256 sequences (N=32768, d=128, fp64 token-by-token recurrence), "
-                  f"{passes} passes in {dt:.2f} s; {head_tokens * 4 * d * d / dt / 1e9:.1f} GFLOP/s fp64",
+        "sample": f"prefill workload batch entry 0 (64 of the 256 sequences, N=32768, d=128), the GPU's own "
+                  f"inputs and initial states, fp64 token-by-token recurrence, median of {reps} runs "
+                  f"({head['seconds_median']:.2f} s each, {head['gflops_fp64']:.1f} GFLOP/s fp64)",
+        "configs": configs,
     }
+    return baseline, errors
 
 
 LONG = dict(B=1, H=64, N=1 << 20, d=128, block=128)
@@ -256,27 +330,35 @@ def decode_steps(la, synth, torch, reps: int = 5):
             "bf16_state_outputs_vs_fp32_state_outputs_rel_err": o_err}
 
 
-def long_context(la, synth, torch, steps: int = 5):
-    """The 1M-token prefill over 64 heads from a zero state: lin_attn_prefill
-    (64 sequences; the value columns split 4 ways to fill the GPU) against
-    lin_attn_prefill_seqsplit (each sequence cut into 4 parts whose initial
-    states come from the token-split K^T V of the parts before).  HIP events
-    on the launch stream, `steps` timed launches after one untimed one; the
-    state is reset outside the timed region."""
+LONG_HEADS = (0, 21, 42, 63)  # heads of the long-context workload checked against the oracle
+
+
+def long_context(la, synth, torch, steps: int = 5, keep_sample: bool = False):
+    """The 1M-token prefill over 64 heads from a zero state, two ways:
+    lin_attn_prefill (64 sequences; the value columns split 4 ways to fill
+    the GPU) and lin_attn_prefill_seqsplit (each sequence cut into parts whose
+    initial states come from the token-split K^T V of the parts before).  HIP
+    events on the launch stream, `steps` timed launches after one untimed
+    one; the state is reset outside the timed region.  With keep_sample, the
+    inputs, outputs and final states of heads LONG_HEADS (batch entry 0) of
+    the last launch of each way are returned as host arrays for the oracle
+    leg."""
     L = LONG
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     q, k, v = synth.prefill_inputs_device(8, L["B"], L["H"], L["N"], L["d"])
     o = torch.empty_like(q)
     S = torch.zeros((L["B"], L["H"], L["d"], L["d"]), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(16, la.prefill_seqsplit_workspace(L["B"], L["H"], L["N"], L["d"], L["block"],
-                                                           torch.bfloat16)), dtype=torch.uint8, device=dev)
-    res = {}
+    ws_bytes = la.prefill_seqsplit_workspace(L["B"], L["H"], L["N"], L["d"], L["block"], torch.bfloat16)
+    ws = torch.empty(max(16, ws_bytes), dtype=torch.uint8, device=dev)
+    hs = list(LONG_HEADS)
+    res, sample = {}, {}
     for name, fn in (("value_split", lambda: la.prefill(q, k, v, o, S, L["block"])),
                      ("seqsplit", lambda: la.prefill_seqsplit(q, k, v, o, S, L["block"], ws))):
         ms = []
         for i in range(steps + 1):
             S.zero_()
+            o.zero_()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()
@@ -284,39 +366,90 @@ def long_context(la, synth, torch, steps: int = 5):
             torch.cuda.synchronize()
             if i > 0:
                 ms.append(e0.elapsed_time(e1))
-        res[name] = sum(ms) / len(ms)
+        res[name] = sorted(ms)[len(ms) // 2]
+        if keep_sample:
+            sample[name] = (o[0, hs].float().cpu().numpy(), S[0, hs].cpu().numpy())
+    if keep_sample:
+        sample["inputs"] = tuple(t[0, hs].float().cpu().numpy() for t in (q, k, v))
+    del q, k, v, o, ws
     tokens = L["B"] * L["N"]
     nbytes = prefill_bytes(**L)
-    return {"metric": "long-context prefill time (ms per launch)",
-            "config": {"workload": "B=1 H=64 N=1048576 d=128 block=128, bf16 q/k/v/o, fp32 state from zero"},
-            "value_split_ms": res["value_split"], "seqsplit_ms": res["seqsplit"],
-            "seqsplit_tokens_per_s": tokens / (res["seqsplit"] / 1e3),
-            "seqsplit_algorithmic_GBps": nbytes / (res["seqsplit"] / 1e3) / 1e9,
-            "value_split_tokens_per_s": tokens / (res["value_split"] / 1e3),
-            "algorithmic_bytes": nbytes,
-            "seqsplit_workspace_bytes": ws.numel()}
+    B, H, N, d = L["B"], L["H"], L["N"], L["d"]
+    out = {"metric": "long-context prefill time (ms per launch, median)",
+           "config": {"workload": "B=1 H=64 N=1048576 d=128 block=128, bf16 q/k/v/o, fp32 state from zero"},
+           "steps": steps, "algorithmic_bytes": nbytes, "seqsplit_workspace_bytes": ws_bytes}
+    for name in ("seqsplit", "value_split"):
+        t = res[name] / 1e3
+        out[name] = {"ms": res[name], "tokens_per_s": tokens / t, "algorithmic_GBps": nbytes / t / 1e9,
+                     "pct_hbm_peak": 100 * nbytes / t / 1e9 / PEAK_HBM_GBS,
+                     "tflops_useful": prefill_flops(**L) / t / 1e12}
+    # design bytes of the sequence split: the prefill's bytes plus K and V of
+    # the first P-1 of the P parts read once more by the state pass, plus the
+    # workspace states written and read once
+    parts = seqsplit_parts(B * H, N)
+    extra = B * H * N * 4 * d * (parts - 1) // parts + 2 * ws_bytes
+    out["seqsplit"]["parts"] = parts
+    out["seqsplit"]["design_bytes"] = nbytes + extra
+    out["seqsplit"]["design_GBps"] = (nbytes + extra) / (res["seqsplit"] / 1e3) / 1e9
+    out["value_split"]["design_note"] = ("each of the 4 value slices of a sequence reads all of q and k "
+                                         "(its own quarter of v and o); the slices share an XCD's L2")
+    return (out, sample) if keep_sample else out
 
 
-def hbm_ceiling(torch, reps: int = 5):
-    """Practical HBM ceiling of each traffic mix of the path, from a plain
-    streaming kernel (csrc/hbm_stream.hip, its own library): 16-byte
-    non-temporal loads, consecutive lanes at consecutive addresses, one
-    contiguous run of 4 KiB units per workgroup.  Measured for reads only,
-    for 3 bytes read per byte written (the prefill's mix: q, k, v in, o out)
-    and for 1:1, between two buffers and in place (the decode step reads and
-    writes its state in place), each the best average over grid sizes and
-    store policies, and over 1, 4 or 16 units loaded per wave before their
-    stores.  HIP events on the launch
-    stream, `reps` timed launches after 2 untimed ones."""
+def seqsplit_parts(BH: int, N: int, cus: int = 256) -> int:
+    """Parts per sequence of lin_attn_prefill_seqsplit's plan (the library's
+    own rule, restated for the byte model): the largest power of two P with
+    B*H*P at most the compute-unit count, P dividing N and parts of at least
+    512 tokens."""
+    P = 1
+    while BH * P * 2 <= cus and N % (P * 2) == 0 and N // (P * 2) >= 512:
+        P *= 2
+    return P
+
+
+def hbm_stream_reference(torch, reps: int = 5):
+    """HBM rates a plain streaming kernel reaches for each traffic mix of the
+    path (csrc/hbm_stream.hip, its own library): 16-byte non-temporal loads,
+    consecutive lanes at consecutive addresses.  A reference for the
+    attention kernels' own mixes, not a bound on them (the decode step beats
+    the 1:1 figure).  Measured for reads only, for 3 bytes read per byte
+    written (the prefill's mix: q, k, v in, o out) and for 1:1, between two
+    buffers and in place (the decode step reads and writes its state in
+    place), each the best average over grid sizes and store policies, and
+    over 1, 4 or 16 units loaded per wave before their stores.  The 3:1 mix is
+    also measured with the prefill's own shape (hbm_stream_roles): one
+    workgroup per compute unit, three waves each streaming one input, a
+    fourth streaming the output.  HIP events on the launch stream, `reps`
+    timed launches after 2 untimed ones."""
     lib = ctypes.CDLL(PROBE_LIB)
     lib.hbm_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_stream_roles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p]
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     read_bytes = 6 << 30
     src = torch.ones(read_bytes // 4, dtype=torch.int32, device=dev)
     dst = torch.zeros(3 << 28, dtype=torch.int32, device=dev)  # 3 GiB
     unit = 4096
+
+    def timed(fn, moved, name):
+        ms = []
+        for i in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"streaming probe {name} returned {rc}")
+            if i >= 2:
+                ms.append(e0.elapsed_time(e1))
+        gbs = moved / (sum(ms) / len(ms) / 1e3) / 1e9
+        if gbs > 1.05 * PEAK_HBM_GBS:  # the probe skipped work it was asked to do
+            raise RuntimeError(f"streaming probe {name} measured {gbs:.0f} GB/s, above the HBM peak")
+        return gbs
+
     mixes = {"read_only": (1, 0, read_bytes // unit, False), "r3w1": (3, 1, read_bytes // (3 * unit), False),
              "r1w1": (1, 1, (3 << 30) // unit, False),
              # in place: each 16-byte piece read and written back to the same
@@ -327,28 +460,23 @@ def hbm_ceiling(torch, reps: int = 5):
         moved = units * unit * (rd + wr)
         best = None
         for nt, wgs, batch in itertools.product((0, 1) if wr else (0,), (2048, 8192, 16384), (1, 4, 16)):
-            ms = []
-            for i in range(reps + 2):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                target = src if in_place else dst
-                rc = lib.hbm_stream(src.data_ptr(), target.data_ptr(), units, rd, wr, nt, wgs, batch,
-                                    stream.cuda_stream)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                if rc != 0:
-                    raise RuntimeError(f"hbm_stream returned {rc}")
-                if i >= 2:
-                    ms.append(e0.elapsed_time(e1))
-            gbs = moved / (sum(ms) / len(ms) / 1e3) / 1e9
-            if gbs > 1.05 * PEAK_HBM_GBS:  # the probe skipped work it was asked to do
-                raise RuntimeError(f"hbm_stream {name} batch={batch} measured {gbs:.0f} GB/s, above the HBM peak")
+            target = src if in_place else dst
+            gbs = timed(lambda: lib.hbm_stream(src.data_ptr(), target.data_ptr(), units, rd, wr, nt, wgs, batch,
+                                               stream.cuda_stream), moved, name)
             if best is None or gbs > best[0]:
-                best = (gbs, nt, wgs, batch)
-        out[name + "_GBps"] = best[0]
-        out[name + "_config"] = f"nt_store={best[1]} workgroups={best[2]} batch={best[3]}"
+                best = (gbs, f"nt_store={nt} workgroups={wgs} batch={batch}")
+        out[name + "_GBps"], out[name + "_config"] = best
+    units = read_bytes // (3 * unit)
+    best = None
+    for nt, wgs, depth in itertools.product((0, 1), (256, 512), (8, 16)):
+        gbs = timed(lambda: lib.hbm_stream_roles(src.data_ptr(), dst.data_ptr(), units, nt, wgs, depth,
+                                                 stream.cuda_stream), units * unit * 4, "r3w1_roles")
+        if best is None or gbs > best[0]:
+            best = (gbs, f"nt_store={nt} workgroups={wgs} depth={depth}")
+    out["r3w1_roles_GBps"], out["r3w1_roles_config"] = best
     del src, dst
-    out["kernel"] = "plain streaming kernel, 16-byte non-temporal loads, 256-lane workgroups (csrc/hbm_stream.hip)"
+    out["kernel"] = ("plain streaming kernels, 16-byte non-temporal loads, 256-lane workgroups "
+                     "(csrc/hbm_stream.hip); r3w1_roles: three reading waves and one writing wave per workgroup")
     return out
 
 
@@ -394,7 +522,7 @@ def main():
         print(json.dumps(long_context(la, synth, torch)))
         return
     if args.only == "ceiling":
-        print(json.dumps(hbm_ceiling(torch)))
+        print(json.dumps(hbm_stream_reference(torch)))
         return
     if args.only == "copy":
         # plain copy of a known size, used to calibrate the HBM byte counters
@@ -487,7 +615,16 @@ def main():
                              ("shard_prefill_seqsplit", need["shard"]),
                              ("shard_prefill", need["shard"])) if on]
 
-    def step(evs):
+    # The states are in/out and carry over from step to step; before the last
+    # timed step each is copied (outside every kernel's event pair) so that
+    # the oracle leg can check that step's outputs from the state they started
+    # from.
+    last_in = {}
+
+    def keep(name, t):
+        last_in[name] = t.clone()
+
+    def step(evs, last=False):
         def timed(name, fn):
             if evs is not None:
                 evs[name][0].record(stream)
@@ -495,19 +632,34 @@ def main():
             if evs is not None:
                 evs[name][1].record(stream)
         if need["prefill"]:
+            if last:
+                last_in["prefill_S"] = pS[0].clone()  # batch entry 0: the oracle leg's sample
             timed("prefill", lambda: la.prefill(pq, pk, pv, po, pS, P["block"]))
+            if last:
+                last_in["prefill_o"] = po[0].clone()
+                last_in["prefill_SN"] = pS[0].clone()
             timed("prefill_snapshots", lambda: la.prefill_snapshots(pq, pk, pv, po, pS2, psnap, P["block"],
                                                                     SNAP_EVERY))
             timed("backward", lambda: la.backward(pq, pk, pv, pdo, pdq, pdk, pdv, P["block"], dstate0=pdS0))
         if need["decode"]:
+            if last:
+                keep("decode_S", dS32)
             timed("decode_fp32", lambda: la.decode(dq, dk, dv, do, dS32))
+            if last:
+                keep("decode_o", do)
+                keep("decode_SN", dS32)
             timed("decode_bf16", lambda: la.decode(dq, dk, dv, do, dS16))
             timed("decode_e4m3", lambda: la.decode(dq, dk, dv, do, dS8, state_scale=dscale))
             timed("verify", lambda: la.decode_verify(tq, tk, tv, to, dS32))
             timed("commit", lambda: la.decode_commit(tk, tv, dS32, tacc))
         if need["small"]:
             flush.fill_(0)
+            if last:
+                keep("small_S", sS)
             timed("small_chunked", lambda: la.prefill(sq, sk, sv, so, sS, S["block"]))
+            if last:
+                keep("small_o", so)
+                keep("small_SN", sS)
             flush.fill_(1)
             timed("small_recurrent", lambda: la.prefill_recurrent(sq, sk, sv, so2, sS2))
             flush.fill_(0)
@@ -526,9 +678,9 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         evs = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
-        step(evs)
+        step(evs, last=(i == args.steps - 1))
         evs_all.append(evs)
     end.record(stream)
     torch.cuda.synchronize()
@@ -543,8 +695,16 @@ def main():
             print(f"{n}: avg {avg[n]:.4f} ms, min {best[n]:.4f} ms over {args.steps} launches")
         return
 
-    ceiling = hbm_ceiling(torch)
+    ceiling = hbm_stream_reference(torch)
     steps128 = decode_steps(la, synth, torch)
+    # drop the shard's and the backward's buffers before the 64 GiB long-context inputs
+    if need["shard"]:
+        del hq, hk, hv, ho, ho2, hS0, hS0b, hdS, hdS2, hws, hpws
+    if need["prefill"]:
+        del pdo, pdq, pdk, pdv
+    torch.cuda.empty_cache()
+    long_res = long_context(la, synth, torch, keep_sample=not args.no_cpu_baseline)
+    long_res, long_sample = long_res if isinstance(long_res, tuple) else (long_res, None)
     p_bytes = prefill_bytes(**P)
     p_flops = prefill_flops(**P)
     p_dense = prefill_dense_flops(**P)
@@ -611,9 +771,9 @@ def main():
             "e4m3_state_ms": avg["decode_e4m3"], "e4m3_state_GBps": d8_bytes / (avg["decode_e4m3"] / 1e3) / 1e9,
             "e4m3_state_pct_hbm_peak": 100 * d8_bytes / (avg["decode_e4m3"] / 1e3) / 1e9 / PEAK_HBM_GBS,
             "tokens_per_s_fp32_state": D["B"] / (avg["decode_fp32"] / 1e3),
-            "fp32_state_pct_of_1to1_stream_ceiling": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9
+            "fp32_state_pct_of_1to1_stream_reference": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9
             / ceiling["r1w1_GBps"],
-            "fp32_state_pct_of_in_place_1to1_stream_ceiling": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9
+            "fp32_state_pct_of_in_place_1to1_stream_reference": 100 * d32_bytes / (avg["decode_fp32"] / 1e3) / 1e9
             / ceiling["r1w1_in_place_GBps"],
             "steps_128": steps128,
             "speculative": {
@@ -641,7 +801,7 @@ def main():
             "state_accumulate_tiles_ms": avg["shard_state_accumulate_tiles"],
             "state_accumulate_tiles_GBps": state_accumulate_bytes(**SH)
             / (avg["shard_state_accumulate_tiles"] / 1e3) / 1e9,
-            "state_accumulate_pct_of_read_only_stream_ceiling": 100 * state_accumulate_bytes(**SH)
+            "state_accumulate_pct_of_read_only_stream_reference": 100 * state_accumulate_bytes(**SH)
             / (avg["shard_state_accumulate"] / 1e3) / 1e9 / ceiling["read_only_GBps"],
             "prefill_nonzero_S0_ms": avg["shard_prefill"],
             "prefill_nonzero_S0_GBps": prefill_bytes(**SH) / (avg["shard_prefill"] / 1e3) / 1e9,
@@ -662,16 +822,23 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes": p_bytes,
             # the best rate a plain streaming kernel reaches for the same 3:1
-            # read:write mix on this GPU (hbm_ceiling), and the share of it
-            "practical_peak_same_mix": ceiling["r3w1_GBps"],
-            "frac_of_practical_peak": gbs / ceiling["r3w1_GBps"],
+            # read:write mix on this GPU (hbm_stream_reference): context, not
+            # a bound (8 TB/s is the peak frac is taken against)
+            "same_mix_stream_reference_GBps": max(ceiling["r3w1_GBps"], ceiling["r3w1_roles_GBps"]),
+            "frac_of_same_mix_stream_reference": gbs / max(ceiling["r3w1_GBps"], ceiling["r3w1_roles_GBps"]),
         },
-        "hbm_ceiling": ceiling,
+        "long": long_res,
+        "hbm_stream_reference": ceiling,
         "timing": {"wall_ms_timed_region": wall_ms, "setup_s": setup_s,
                    "method": "HIP events on the launch stream around each kernel"},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"], out["error_vs_oracle"] = cpu_baseline(
+            (pq[0], pk[0], pv[0], last_in["prefill_S"], last_in["prefill_o"], last_in["prefill_SN"]),
+            (sq, sk, sv, last_in["small_S"], last_in["small_o"], last_in["small_SN"]),
+            (dq, dk, dv, last_in["decode_S"], last_in["decode_o"], last_in["decode_SN"]),
+            long_sample)
+        out["error_vs_oracle"]["gates"] = {"bf16_io_fp32_state": 1e-2, "fp32_io": 1e-4}
     print(json.dumps(out))
 
 

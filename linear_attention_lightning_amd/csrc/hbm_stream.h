@@ -1,5 +1,6 @@
-/* Streaming bandwidth probe (measurement only; not part of the attention
- * library, built separately as libhbm_stream.so).
+/* Streaming bandwidth probes (measurement only; not part of the attention
+ * library, built separately as libhbm_stream.so): reference rates for a
+ * read:write mix, not bounds on the attention kernels.
  *
  * hbm_stream: one launch of a plain streaming kernel on `stream`.
  *   src, dst      device pointers, 16-byte aligned, owned by the caller; with
@@ -28,6 +29,15 @@ extern "C" {
 
 int hbm_stream(const void *src, void *dst, int64_t units, int reads_per_write, int write, int nt_store,
                int workgroups, int batch, hipStream_t stream);
+/* hbm_stream_roles: the prefill's traffic shape.  Each workgroup of 4 waves
+ * takes a contiguous run of `units` (ceil(units / workgroups) each): waves
+ * 0..2 read that run of the first, second and third third of src (src holds
+ * 3 * units * 4096 bytes), `depth` 16-byte loads per lane in flight (4, 8 or
+ * 16), and wave 3 writes that run of dst (units * 4096 bytes) with a fixed
+ * pattern.  src and dst must differ.  Same return codes as hbm_stream.
+ */
+int hbm_stream_roles(const void *src, void *dst, int64_t units, int nt_store, int workgroups, int depth,
+                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

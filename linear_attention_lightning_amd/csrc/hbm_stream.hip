@@ -1,5 +1,6 @@
-// Streaming kernel that measures the HBM bandwidth a plain, well-coalesced
-// kernel reaches for a given read:write byte mix.  It is measurement
+// Streaming kernels that measure the HBM bandwidth a plain, well-coalesced
+// kernel reaches for a given read:write byte mix (a reference rate for the
+// attention kernels' own mixes; not a bound on them).  It is measurement
 // infrastructure, not part of the attention library: bench.py loads it (as
 // _lib/libhbm_stream.so) to put the attention kernels' rates beside the
 // practical ceiling of their own traffic mix (the prefill reads three bytes
@@ -110,7 +111,61 @@ int dispatch(const void *src, void *dst, int64_t units, int rd, int write, int n
   return 0;
 }
 
+// Role-split stream, the traffic shape of the prefill (one workgroup per
+// compute unit streaming three inputs in and one output out): in each
+// workgroup of 4 waves, wave w < 3 reads units [u0, u1) of the w-th third of
+// src (DEPTH 16-byte loads per lane in flight) and wave 3 writes units
+// [u0, u1) of dst with a fixed pattern.  The reads feed a store that equal
+// bytes never take, so they cannot be dropped.
+template <int DEPTH, bool NT_STORE>
+__global__ __launch_bounds__(256) void roles_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                     int64_t units, int64_t per_wg, unsigned salt) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t u0 = (int64_t)blockIdx.x * per_wg;
+  const int64_t u1 = u0 + per_wg < units ? u0 + per_wg : units;
+  if (u0 >= u1) return;
+  const int64_t n = (u1 - u0) * 256;  // 16-byte pieces of the run
+  if (wave < 3) {
+    const u32x4 *s = src + ((int64_t)wave * units + u0) * 256 + lane;
+    u32x4 acc = {salt, salt, salt, salt};
+    int64_t i = 0;
+    for (; i + 64 * DEPTH <= n; i += 64 * DEPTH) {
+      u32x4 x[DEPTH];
+#pragma unroll
+      for (int b = 0; b < DEPTH; ++b) x[b] = __builtin_nontemporal_load(s + i + 64 * b);
+#pragma unroll
+      for (int b = 0; b < DEPTH; ++b) acc ^= x[b];
+    }
+    for (; i < n; i += 64) acc ^= __builtin_nontemporal_load(s + i);
+    if (acc[0] != acc[1]) dst[lane] = acc;
+  } else {
+    u32x4 *d = dst + u0 * 256 + lane;
+    const u32x4 v = {salt ^ 0x9e3779b9u, salt ^ 0x7f4a7c15u, salt ^ 0x94d049bbu, salt ^ 0x2545f491u};
+    for (int64_t i = 0; i < n; i += 64) put<NT_STORE>(d + i, v);
+  }
+}
+
+template <int DEPTH>
+void launch_roles(const void *src, void *dst, int64_t units, int nt, int wgs, hipStream_t stream) {
+  const int64_t per = (units + wgs - 1) / wgs;
+  if (nt)
+    roles_kernel<DEPTH, true><<<wgs, 256, 0, stream>>>((const u32x4 *)src, (u32x4 *)dst, units, per, 0u);
+  else
+    roles_kernel<DEPTH, false><<<wgs, 256, 0, stream>>>((const u32x4 *)src, (u32x4 *)dst, units, per, 0u);
+}
+
 }  // namespace
+
+extern "C" int hbm_stream_roles(const void *src, void *dst, int64_t units, int nt_store, int workgroups, int depth,
+                                hipStream_t stream) {
+  if (!src || !dst || units < 0 || workgroups <= 0 || src == dst) return -1;
+  if (depth != 4 && depth != 8 && depth != 16) return -2;
+  if (units == 0) return 0;
+  if (depth == 4) launch_roles<4>(src, dst, units, nt_store, workgroups, stream);
+  else if (depth == 8) launch_roles<8>(src, dst, units, nt_store, workgroups, stream);
+  else launch_roles<16>(src, dst, units, nt_store, workgroups, stream);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" int hbm_stream(const void *src, void *dst, int64_t units, int reads_per_write, int write,
                           int nt_store, int workgroups, int batch, hipStream_t stream) {

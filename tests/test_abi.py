@@ -303,6 +303,12 @@ def test_stream_probe_is_a_separate_library():
     assert lib.hbm_stream(FAKE, FAKE, 1, 3, 1, 0, 1, 1, None) == -2  # in place needs one read per write
     assert lib.hbm_stream(FAKE, FAKE, 1, 1, 0, 0, 1, 1, None) == -2  # an in-place run must write
     assert lib.hbm_stream(FAKE, FAKE, 1, 1, 1, 0, 1, 2, None) == -2  # batch is 1, 4 or 16
+    lib.hbm_stream_roles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p]
+    assert lib.hbm_stream_roles(None, FAKE, 1, 0, 1, 8, None) == -1
+    assert lib.hbm_stream_roles(FAKE, FAKE, 1, 0, 1, 8, None) == -1      # src and dst must differ
+    assert lib.hbm_stream_roles(FAKE, FAKE + 16, 1, 0, 1, 5, None) == -2  # depth is 4, 8 or 16
+    assert lib.hbm_stream_roles(FAKE, FAKE + 16, 0, 0, 1, 8, None) == 0   # nothing to do: no launch
     nm = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True, check=True)
     assert "hbm_stream" not in nm.stdout
 

@@ -71,3 +71,22 @@ def test_read_only_stream_stores_nothing_for_equal_bytes(batch):
     run(lib, src, dst, 1, 0, 0, batch)
     # equal bytes everywhere: the guarded store never happens
     assert torch.all(dst == 7)
+
+
+@pytest.mark.parametrize("nt,depth", list(itertools.product((0, 1), (4, 8, 16))))
+def test_role_split_stream_writes_its_pattern_and_reads_everything(nt, depth):
+    """The role-split reference (three reading waves, one writing wave per
+    workgroup) fills every written unit with its pattern, and its reads of
+    equal bytes never take the guarded store."""
+    announce("stream probe roles", nt, depth)
+    lib = probe()
+    lib.hbm_stream_roles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p]
+    src = torch.ones((3 * UNITS * UNIT // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.full((UNITS * UNIT // 4,), 7, dtype=torch.int32, device="cuda")
+    rc = lib.hbm_stream_roles(src.data_ptr(), dst.data_ptr(), UNITS, nt, WORKGROUPS, depth,
+                              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    pattern = torch.tensor([0x9e3779b9, 0x7f4a7c15, 0x94d049bb, 0x2545f491], dtype=torch.int64).to(torch.int32)
+    assert torch.equal(dst.view(-1, 4).cpu(), pattern.expand(UNITS * UNIT // 16, 4))
