@@ -467,6 +467,22 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       }
   };
 
+  // Per-lane parts of the Q-row load and output-store offsets (bytes),
+  // computed once.  A Q-row load gives lane (lr, g) row r = lr mod 8 (+ 8 h)
+  // of a row tile and 16 bytes at element 16 g + 8 (lr / 8) of a 128-byte
+  // line; a quad store gives it token lr mod 8 (+ 8 h) and bytes
+  // 64 (lr / 8) + 16 g of a 128-byte piece.  Reversed order puts row r of a
+  // block at len - 1 - r: the per-lane part is then -r D.
+  const int q_lane = [&] {
+    const LaneOff lo = lane_off();
+    const int col = 16 * lo.g + 8 * (lo.lr >> 3);
+    return ((REV ? -(lo.lr & 7) : (lo.lr & 7)) * D + col) * 2;
+  }();
+  const int st_lane = [&] {
+    const LaneOff lo = lane_off();
+    return (REV ? -(lo.lr & 7) : (lo.lr & 7)) * D * 2 + (lo.lr >> 3) * 64 + 16 * lo.g;
+  }();
+
   // ---- Q rows of the wave's two row tiles (registers) ----
   bf16x8 bq[2][P::NKC], qn[2][P::NKC];
   bf16x8 qv[2][P::NKC];  // fused dK/dV: the block's v rows (the dK role's queries)
@@ -487,22 +503,19 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const u32x4 dq = raw_desc((vrows ? qh2 : qh) + (size_t)tok0 * D, act ? (uint32_t)len * D * 2 : 0u);
     __amdgpu_buffer_rsrc_t rq;
     __builtin_memcpy(&rq, &dq, sizeof(rq));
-    const LaneOff lo = lane_off();
     const int l = m >> 1, h = m & 1;
-    const int col = 16 * lo.g + 8 * (lo.lr >> 3);  // element within the line
     if constexpr (REV) {
       // row 16 T + r is token len-1-16T-r of the span (negative: padding)
-      const int qrow = len - 1 - 16 * (u ? T1 : T0) - 8 * h - (lo.lr & 7);
+      const int qoff = q_lane + (len - 1 - 16 * (u ? T1 : T0) - 8 * h) * D * 2;
       const bf16x8 x = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rq, (qrow * D + col) * 2, l * 128, 2));
+                                                 rq, qoff, l * 128, 2));
       if (vrows)
         qv[u][m] = x;
       else
         qn[u][m] = x;
     } else {
-      const int qlane = ((lo.lr & 7) * D + col) * 2;
       qn[u][m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rq, qlane, ((16 * (u ? T1 : T0) + 8 * h) * D + 64 * l) * 2, 2));
+                                               rq, q_lane, ((16 * (u ? T1 : T0) + 8 * h) * D + 64 * l) * 2, 2));
     }
   };
   // Operand fragments from the loaded lines.  Step 2l (chunk 2g of line l for
@@ -631,23 +644,25 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // products of step kc; the first key chunk's operands during the last two.
     bf16x8 sfr[P::NKC][P::NJC];
     auto load_s = [&](int kc) __attribute__((always_inline)) {
+      if constexpr (TS) {
+        // A = S itself: lane (i, g) needs S[16 (jc0 + jl) + i][8 tau + e],
+        // tau = 8 (kc / 2) + 2 g + kc % 2 (the head-dimension order of the
+        // query fragments), i.e. column 16 (jc0 + jl) + i of rows
+        // 8 tau + e of the copy: two transposing reads whose 16 lanes
+        // address rows 8 tau + lr / 4 (+ 4) and columns + 4 (lr % 4).  The
+        // lane's rows and its swizzle bits are formed once per step: a
+        // row's swizzle is an XOR with bits of the row mod 16, and the
+        // value tiles only change the logical chunk's upper bits.
+        const LaneOff lt = lane_off();
+        const int r0 = 8 * (8 * (kc >> 1) + 2 * lt.g + (kc & 1)) + (lt.lr >> 2), r1 = r0 + 4;
+        const int b0 = r0 * RB + lt.lo8, b1 = r1 * RB + lt.lo8;
+        const int x0 = swz<P::CPRK>(r0, lt.h) << 4, x1 = swz<P::CPRK>(r1, lt.h) << 4;
 #pragma unroll
-      for (int jl = 0; jl < P::NJC; ++jl) {
-        if constexpr (TS) {
-          // A = S itself: lane (i, g) needs S[16 (jc0 + jl) + i][8 tau + e],
-          // tau = 8 (kc / 2) + 2 g + kc % 2 (the head-dimension order of the
-          // query fragments), i.e. column 16 (jc0 + jl) + i of rows
-          // 8 tau + e of the copy: two transposing reads whose 16 lanes
-          // address rows 8 tau + lr / 4 (+ 4) and columns + 4 (lr % 4)
-          const LaneOff lt = lane_off();
-          const int tau = 8 * (kc >> 1) + 2 * lt.g + (kc & 1);
-          const int r0 = 8 * tau + (lt.lr >> 2), r1 = r0 + 4;
-          const int ch = 2 * (jc0 + jl) + lt.h;
-          sfr[kc][jl] = ldtr(SsT, r0 * RB + (swz<P::CPRK>(r0, ch) << 4) + lt.lo8,
-                             r1 * RB + (swz<P::CPRK>(r1, ch) << 4) + lt.lo8);
-        } else {
-          sfr[kc][jl] = ld128(SsT, kf[kc] + (jc0 + jl) * 16 * RB);
-        }
+        for (int jl = 0; jl < P::NJC; ++jl)
+          sfr[kc][jl] = ldtr(SsT, b0 + ((32 * (jc0 + jl)) ^ x0), b1 + ((32 * (jc0 + jl)) ^ x1));
+      } else {
+#pragma unroll
+        for (int jl = 0; jl < P::NJC; ++jl) sfr[kc][jl] = ld128(SsT, kf[kc] + (jc0 + jl) * 16 * RB);
       }
     };
     load_s(0);
@@ -809,9 +824,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       const auto y2 = __builtin_amdgcn_permlane16_swap(y1[0], y1[1], false, false);
       pr[h] = u32x4{x2[0], y2[0], x2[1], y2[1]};
     }
-    const LaneOff lo_st = lane_off();
-    const bool upper = lo_st.lr >= 8;
-    const int col = (jc0 * 16) * 2 + jq * 128 + (lo_st.lr >> 3) * 64 + 16 * lo_st.g;  // byte in the slice row
+    const bool upper = (lane_now() & 15) >= 8;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // store h: the lower lanes keep pair A (h = 0) or take the partner's
@@ -823,12 +836,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int moved = __builtin_amdgcn_update_dpp(0, (int)pr[1 - h][w], 0x128 /* row_ror:8 */, 0xf, 0xf, false);
         data[w] = (upper == (h == 0)) ? (uint32_t)moved : pr[h][w];
       }
-      const int tok = 8 * h + (lo_st.lr & 7);  // token within the row tile
+      // token 8 h + lr mod 8 of the row tile, bytes 64 (lr / 8) + 16 g of
+      // piece jq of the slice row
+      const int cst = (jc0 * 16) * 2 + jq * 128;
       if constexpr (REV) {
-        const int orow = len - 1 - 16 * (u ? T1 : T0) - tok;
-        __builtin_amdgcn_raw_buffer_store_b128(data, ro, orow * D * 2 + col, 0, kStNT);
+        __builtin_amdgcn_raw_buffer_store_b128(data, ro, st_lane + (len - 1 - 16 * (u ? T1 : T0) - 8 * h) * D * 2 + cst,
+                                               0, kStNT);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b128(data, ro, tok * D * 2 + col, 16 * (u ? T1 : T0) * D * 2, kStNT);
+        __builtin_amdgcn_raw_buffer_store_b128(data, ro, st_lane + 8 * h * D * 2 + cst, 16 * (u ? T1 : T0) * D * 2,
+                                               kStNT);
       }
     }
   };

@@ -76,10 +76,10 @@ def test_decode_bf16_state_matches_bf16_storage_model(d):
     flips = 0
     for step in range(steps):
         q, k, v = synth.decode_step_inputs(step, B, H, d)
-        o_ref = oracle.decode_step_bf16_state(q, k, v, Sb_ref)
         # the exact pre-store state: the stored values plus k v^T in fp64
         S_exact = oracle.recurrence(q[:, :, None], k[:, :, None], v[:, :, None],
                                     oracle.bf16_bits_to_f64(Sb_ref))[1]
+        o_ref = oracle.decode_step_bf16_state(q, k, v, Sb_ref.copy())  # (updates its argument in place)
         od = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
         la.decode(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), od, Sb)
         torch.cuda.synchronize()
