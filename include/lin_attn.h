@@ -338,23 +338,38 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state,
  * state), computed as follows.  Each sequence's N tokens are cut into P equal
  * parts so that B*H*P is at most the device's compute-unit count (one
  * chunked-prefill workgroup per compute unit, before any value-column split;
- * parts of at least 512 tokens, P a power of two dividing N).  The
- * K^T V of the first P-1 parts is summed by the token-split accumulation
- * (into the workspace); each part's initial state is S_0 plus the sums of the
- * parts before it, added in part order (the associativity equation of
- * [ZENN], section "線形アテンションの数学的基礎": the state after a
- * concatenation is the sum of the segments' K^T V); the parts then run as
- * B*H*P independent prefills, and the last part's final state is written to
- * state.  This reads K and V once more for (P-1)/P of the tokens and in
- * exchange fills the GPU where B*H alone would leave compute units idle.
- * When P = 1 (enough sequences, short or indivisible N, or fp32 I/O) the
- * call is lin_attn_prefill and needs no workspace.
+ * parts of at least 256 tokens, P a power of two dividing N).  Each part
+ * starts from S_0 plus the K^T V sums of the parts before it, added in part
+ * order (the associativity equation of [ZENN], section
+ * "線形アテンションの数学的基礎": the state after a concatenation is the sum
+ * of the segments' K^T V), and runs as a chunked prefill; the last part of
+ * each sequence writes the final state to state.
+ *  - d = 128 and P <= 32: one launch.  Each part but the last first sums K^T V over its
+ *    own tokens and publishes the sum; the parts of a sequence then form the
+ *    start states together (each for 1/P of the state's elements) and
+ *    publish them; each part reads its own start and runs.  Parts wait for
+ *    one another through flags in the workspace, which hold a per-call
+ *    random 64-bit value when set; a wait longer than about one second
+ *    (only possible when the parts of a launch cannot all run, e.g. a device
+ *    shared with a kernel that never yields) gives NaN outputs instead of
+ *    hanging.
+ *  - otherwise two launches.  The token-split accumulation sums the K^T V of
+ *    the first P-1 parts into the workspace (which also receives a copy of
+ *    S_0); the parts then run as B*H*P prefills, each adding the sums of the
+ *    parts before it itself.
+ * Both read K and V once more for (P-1)/P of the tokens, and in exchange
+ * fill the GPU where B*H alone would leave compute units idle.  When P = 1
+ * (enough sequences, short or indivisible N, or fp32 I/O) the call is
+ * lin_attn_prefill and needs no workspace.
  *
  * lin_attn_prefill_seqsplit_workspace returns the workspace bytes the call
- * needs on the current device (the plan depends on its compute-unit count),
- * (2P - 1 + (P-1)(S-1)) * B*H * d*d * 4 for S <= 4 accumulation chunks per
- * part (0 when P = 1), or a negative error code for arguments the call
- * rejects (LIN_ATTN_EHIP when the device cannot be queried).
+ * needs on the current device (the plan depends on its compute-unit count):
+ * 2 (P-1) * B*H * d*d * 4 + 96 * B*H*P for one launch, ((P-1) S + 1) * B*H
+ * * d*d * 4 for two launches with S <= 4 accumulation chunks per part, 0
+ * when P = 1; or a negative error code for arguments the call rejects
+ * (LIN_ATTN_EHIP when the device cannot be queried).  The workspace's
+ * contents on entry do not matter, and a call leaves its flag words zero;
+ * calls that overlap in time must not share a workspace.
  * workspace, workspace_bytes: as lin_attn_state_accumulate_split.  Other
  * arguments, layouts and errors as lin_attn_prefill.
  */
@@ -373,12 +388,14 @@ int lin_attn_prefill_seqsplit(const void *q, const void *k, const void *v, void 
  * buffer inside the library instead of an argument.  The call allocates
  * nothing (no hipMalloc, no hipFree, no allocating library routine).
  *
- * The buffer: lin_attn_scratch_bytes() bytes (64 MiB) of device memory per
+ * The buffer: lin_attn_scratch_bytes() bytes (56 MiB) of device memory per
  * device the library runs on, held from the library's load until the process
  * ends.  Its device address is looked up once per device, on the first call
  * on that device.  Every call on a device uses that device's one buffer, and
  * nothing in it needs to start at zero: each byte the kernels read was written
- * earlier in the same call.  Calls that overlap in time on one device
+ * earlier in the same call, except the one-launch plan's flag words, which
+ * count as set only when they hold that call's random 64-bit value (and
+ * which each call leaves zero).  Calls that overlap in time on one device
  * (different streams, or different host threads) therefore race on the
  * buffer and give wrong results: serialise them, e.g. on one stream.
  *

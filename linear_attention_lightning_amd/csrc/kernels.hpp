@@ -43,7 +43,29 @@ struct PrefillArgs {
   const float *g_in2;
   float *g_out2;
   int g_in_t2;
+  // one part of a sequence cut along the tokens (prefill_bf16_part_launch):
+  // the launch's BH sequences are part_BH sequences of part_P parts each
+  // (sequence index = seq * part_P + p); part p starts from part_s0[seq] plus
+  // part_sums[c * part_BH + seq] for c < p * part_S, added in that order, and
+  // the last part writes its final state to state[seq] (the others to nowhere)
+  const float *part_s0;
+  const float *part_sums;
+  int64_t part_BH;
+  int part_P, part_S;
+  // one-launch form (prefill_bf16_part_lb_launch, d = 128, part_P <= kPartMaxOneLaunch):
+  // part_sums_w (= part_sums) holds 2 (part_P - 1) part_BH d^2 floats: the
+  // K^T V of parts 0 .. P-2, then the start states of parts 1 .. P-1, each
+  // [part][seq][d^2] in the workgroups' fragment order.  part_flags holds
+  // three arrays of part_BH * part_P * kPartMaxSplit words (published,
+  // slab, done; [seq][part][slice]), set to part_epoch in turn; the last part
+  // clears the words of its slice once every other part is done, so a call
+  // leaves the words it used zero.
+  float *part_sums_w;
+  unsigned long long *part_flags;
+  unsigned long long part_epoch;
 };
+constexpr int kPartMaxSplit = 4;
+constexpr int kPartMaxOneLaunch = 32;
 // Two reversed gradient passes of the same BH sequences in one launch: pass
 // 1 from the q, k, v, o, g_* pointers, pass 2 from the *2 pointers.  The
 // two passes must read the same key and value tensors (k2, v2 = v, k); the
@@ -58,6 +80,9 @@ hipError_t prefill_bf16_grad_fused_launch(PrefillArgs a, int64_t BH, int d, hipS
 int prefill_bf16_max_block(int d);
 int prefill_bf16_max_split(int d);
 hipError_t prefill_bf16_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
+// the parts of sequences cut along the tokens (PrefillArgs part_*): BH = part_BH * part_P
+hipError_t prefill_bf16_part_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
+hipError_t prefill_bf16_part_lb_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream);
 // state_fmt: kStBF16 or kStE4M3
 hipError_t prefill_bf16_scaled_launch(PrefillArgs a, int64_t BH, int d, int state_fmt, hipStream_t stream);
 // reverse: walk the sequence from its end (suffix sums)
@@ -146,21 +171,15 @@ struct StateSplitArgs {
   float *partial;               // [(chunks-1) BH][d][d]
   int64_t N, BH, chunks, chunk_len;
   // non-zero: every chunk c starts from zero and writes partial[c BH + bh]
-  // (partial then holds chunks BH states; state is not touched)
+  // (partial then holds chunks BH states; state is not touched except that
+  // the chunk-0 workgroup of each sequence copies state[bh] to s0_copy[bh]
+  // when s0_copy is not null)
   int all_partial;
+  float *s0_copy;
 };
 hipError_t state_split_launch(StateSplitArgs a, int d, hipStream_t stream);
 // chunks and chunk length (a multiple of 64) for BH sequences of N >= 1 tokens
 // on a device of `cus` compute units
 void state_split_plan(int64_t BH, int64_t N, int cus, int64_t *chunks, int64_t *chunk_len);
-
-// Initial states of the P parts of each sequence for a prefill cut along the
-// tokens: starts[bh P + p] = state[bh] + sum over chunks c < p S of
-// partial[c BH + bh] (in chunk order), for p = 0 .. P-1; [d][d] fp32 each.
-hipError_t state_part_starts_launch(const float *state, const float *partial, float *starts, int64_t BH,
-                                    int64_t P, int64_t S, int d, hipStream_t stream);
-// state[bh] = starts[bh P + P - 1] (the final state of each sequence's last part)
-hipError_t state_take_last_launch(const float *starts, float *state, int64_t BH, int64_t P, int d,
-                                  hipStream_t stream);
 
 }  // namespace lal

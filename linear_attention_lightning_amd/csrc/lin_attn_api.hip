@@ -4,6 +4,8 @@
 // Every check that can reject a call runs on the host before the first HIP
 // call, so invalid arguments never reach the device.
 #include <atomic>
+#include <chrono>
+#include <random>
 
 #include "kernels.hpp"
 #include "lin_attn.h"
@@ -13,7 +15,7 @@
 // the name is a host-side stand-in, not a device address: the address of each
 // device's copy comes from hipGetSymbolAddress (scratch_ptr below), and only
 // that address is passed to kernels.
-constexpr int64_t kScratchBytes = 64ll << 20;
+constexpr int64_t kScratchBytes = 56ll << 20;
 static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
 
 namespace {
@@ -469,19 +471,30 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state, 
   if (!ok_ptr(k) || !ok_ptr(v) || !ok_ptr(state)) return LIN_ATTN_EINVAL;
   if (ws > 0 && !ok_ptr(workspace)) return LIN_ATTN_EINVAL;
   lal::StateSplitArgs a{(const unsigned short *)k, (const unsigned short *)v, state, (float *)workspace,
-                        N, BH, chunks, chunk_len, 0};
+                        N, BH, chunks, chunk_len, 0, nullptr};
   return from_hip(lal::state_split_launch(a, (int)d, (hipStream_t)stream));
 }
 
 namespace {
 
 // Prefill cut along the tokens: P parts per sequence (B*H*P at most the
-// device's compute units, parts of at least 512 tokens, P a power of two
-// dividing N); the K^T V of the first P-1 parts is summed in chunks of L/S
-// tokens (S a power of two <= 4 dividing L, chunks of at least 1024 tokens).
-// Workspace: (P-1) S BH partial states, then BH P part states.
+// device's compute units, parts of at least 256 tokens, P a power of two
+// dividing N) of L = N/P tokens.
+//  - At d = 128, up to kPartMaxOneLaunch parts run in one launch: each part
+//    but the last sums its own K^T V and publishes it, and the parts then
+//    form every part's start state together, each for 1/P of the elements.
+//    Workspace: 2 (P-1) BH states, then three flag arrays of BH P
+//    kPartMaxSplit 64-bit words.  (At d = 64 the states are a quarter of the
+//    size, the two launches' cached reads of them are cheap, and the
+//    exchanges between parts would cost more than the launch they save.)
+//  - Otherwise two launches: the K^T V of the first P-1 parts is
+//    summed in chunks of L/S tokens (S a power of two <= 4 dividing L, chunks
+//    of at least 1024 tokens) by a pass of (P-1) S BH workgroups.
+//    Workspace: (P-1) S BH partial states, then a copy of the BH initial
+//    states.
 struct SeqSplitPlan {
   int64_t BH, P, L, S, ws_bytes;
+  bool one_launch;
 };
 
 int seqsplit_check(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype,
@@ -502,12 +515,18 @@ int seqsplit_check(int64_t B, int64_t H, int64_t N, int64_t d, int64_t block, li
     int cus = 0;
     const int rc = cu_count(&cus);
     if (rc != LIN_ATTN_OK) return rc;
-    while (BH * pl->P * 2 <= cus && N % (pl->P * 2) == 0 && N / (pl->P * 2) >= 512) pl->P *= 2;
+    while (BH * pl->P * 2 <= cus && N % (pl->P * 2) == 0 && N / (pl->P * 2) >= 256) pl->P *= 2;
   }
   pl->L = pl->P > 0 ? N / pl->P : N;
-  if (pl->P > 1) {
+  pl->one_launch = pl->P > 1 && pl->P <= lal::kPartMaxOneLaunch && d == 128;
+  if (pl->one_launch) {
+    int64_t states, flags;
+    if (!mul_ok(2 * (pl->P - 1) * BH, d * d * 4, &states) || !mul_ok(BH * pl->P, 3 * lal::kPartMaxSplit * 8, &flags))
+      return LIN_ATTN_EINVAL;
+    pl->ws_bytes = states + flags;
+  } else if (pl->P > 1) {
     while (pl->S < 4 && pl->L % (pl->S * 2) == 0 && pl->L / (pl->S * 2) >= 1024) pl->S *= 2;
-    const int64_t states = (pl->P - 1) * pl->S * BH + BH * pl->P;
+    const int64_t states = (pl->P - 1) * pl->S * BH + BH;
     if (!mul_ok(states, d * d * 4, &pl->ws_bytes)) return LIN_ATTN_EINVAL;
   }
   return LIN_ATTN_OK;
@@ -524,29 +543,75 @@ int64_t lin_attn_prefill_seqsplit_workspace(int64_t B, int64_t H, int64_t N, int
 
 namespace {
 
+// A 64-bit value that differs from call to call (and from what a workspace
+// is likely to hold): a random seed plus a call counter, through the
+// splitmix64 finalizer (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", 2014).  Zero is skipped: it is the value
+// of a cleared flag.
+uint64_t next_part_epoch() {
+  static const uint64_t seed = [] {
+    std::random_device rd;
+    return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^
+           (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  }();
+  static std::atomic<uint64_t> calls{0};
+  uint64_t z;
+  do {
+    z = seed + (calls.fetch_add(1, std::memory_order_relaxed) + 1) * 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    z ^= z >> 31;
+  } while (z == 0);
+  return z;
+}
+
 // The launches of a prefill cut along the tokens (plan pl, P > 1), with the
-// workspace at `workspace` (pl.ws_bytes bytes; every byte the kernels read is
-// written by an earlier launch of the same call, so its contents on entry do
-// not matter).
+// workspace at `workspace` (pl.ws_bytes bytes).
+// One-launch plan: the parts as B*H*P sequences of L tokens, each part but
+// the last summing its own K^T V into the workspace first (see
+// kPsPartLB).  The flag words are compared with this call's epoch, so their
+// contents on entry do not matter unless they hold that random 64-bit value;
+// the call leaves the words it used zero.
+// Two-launch plan (every workspace byte read is written earlier in the call):
+//  1. the K^T V sums of the first P-1 parts, (P-1) S chunks per sequence,
+//     into the workspace; the chunk-0 workgroups also copy S_0 there (the
+//     state buffer is overwritten by the last part during launch 2, while
+//     other parts may still be reading their start);
+//  2. the parts as B*H*P sequences of L tokens (contiguous in memory): each
+//     forms its initial state from S_0 and the sums of the parts before it,
+//     in part order, and the last part of each sequence writes S_N.
 int seqsplit_run(const SeqSplitPlan &pl, const void *q, const void *k, const void *v, void *o, float *state,
                  int64_t N, int64_t d, int64_t block, lin_attn_dtype_t io_dtype, void *workspace, void *stream) {
-  int rc;
+  (void)io_dtype;  // bf16: the plan cuts bf16 sequences only
   hipStream_t s = (hipStream_t)stream;
+  const int64_t parts = pl.BH * pl.P;
+  int cus = 0;
+  int rc = cu_count(&cus);
+  if (rc != LIN_ATTN_OK) return rc;
+  int nsplit = 1;
+  while (nsplit < lal::prefill_bf16_max_split((int)d) && parts * nsplit < cus) nsplit *= 2;
+  static_assert(lal::kPartMaxSplit >= 4, "flag arrays hold every value slice");
+  if (parts * nsplit > 0x7fffffff) return LIN_ATTN_EUNSUPPORTED;
+  if (pl.L / block > 0x7ffffff0) return LIN_ATTN_EUNSUPPORTED;
   float *partial = (float *)workspace;
-  float *starts = partial + (size_t)(pl.P - 1) * pl.S * pl.BH * d * d;
-  // 1. K^T V of the first P-1 parts, in (P-1) S chunks per sequence
-  lal::StateSplitArgs a{(const unsigned short *)k, (const unsigned short *)v, state, partial,
-                        N, pl.BH, (pl.P - 1) * pl.S, pl.L / pl.S, 1};
-  rc = from_hip(lal::state_split_launch(a, (int)d, s));
+  lal::PrefillArgs a{};
+  a.q = (const unsigned short *)q; a.k = (const unsigned short *)k; a.v = (const unsigned short *)v;
+  a.o = (unsigned short *)o; a.state = state; a.N = pl.L; a.blk = (int)block; a.nsplit = nsplit;
+  a.part_BH = pl.BH; a.part_P = (int)pl.P; a.part_S = 1;
+  if (pl.one_launch) {
+    a.part_sums = partial;
+    a.part_sums_w = partial;
+    a.part_flags = (unsigned long long *)(partial + 2 * (size_t)(pl.P - 1) * pl.BH * d * d);
+    a.part_epoch = next_part_epoch();
+    return from_hip(lal::prefill_bf16_part_lb_launch(a, parts, (int)d, s));
+  }
+  float *s0_copy = partial + (size_t)(pl.P - 1) * pl.S * pl.BH * d * d;
+  lal::StateSplitArgs sa{(const unsigned short *)k, (const unsigned short *)v, state, partial,
+                         N, pl.BH, (pl.P - 1) * pl.S, pl.L / pl.S, 1, s0_copy};
+  rc = from_hip(lal::state_split_launch(sa, (int)d, s));
   if (rc != LIN_ATTN_OK) return rc;
-  // 2. each part's initial state: S_0 plus the sums of the parts before it
-  rc = from_hip(lal::state_part_starts_launch(state, partial, starts, pl.BH, pl.P, pl.S, (int)d, s));
-  if (rc != LIN_ATTN_OK) return rc;
-  // 3. the parts as B*H*P independent sequences of L tokens (contiguous in memory)
-  rc = prefill_impl(q, k, v, o, starts, nullptr, 0, pl.BH * pl.P, 1, pl.L, d, block, io_dtype, 0, stream);
-  if (rc != LIN_ATTN_OK) return rc;
-  // 4. the final state is the last part's
-  return from_hip(lal::state_take_last_launch(starts, state, pl.BH, pl.P, (int)d, s));
+  a.part_s0 = s0_copy; a.part_sums = partial; a.part_S = (int)pl.S;
+  return from_hip(lal::prefill_bf16_part_launch(a, parts, (int)d, s));
 }
 
 }  // namespace

@@ -12,4 +12,13 @@ hipError_t prefill_bf16_launch(PrefillArgs a, int64_t BH, int d, hipStream_t str
   return a.snap ? prefill_bf16_dispatch<kPsF32Snap>(a, BH, d, stream) : prefill_bf16_dispatch<kPsF32>(a, BH, d, stream);
 }
 
+hipError_t prefill_bf16_part_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream) {
+  return prefill_bf16_dispatch<kPsPart>(a, BH, d, stream);
+}
+
+// d = 128 only: at d = 64 the two-launch form is the faster one
+hipError_t prefill_bf16_part_lb_launch(PrefillArgs a, int64_t BH, int d, hipStream_t stream) {
+  return prefill_bf16_dispatch<kPsPartLB, false>(a, BH, d, stream);
+}
+
 }  // namespace lal

@@ -103,8 +103,23 @@ enum PrefillStateMode {
   // K and V tiles staged in LDS are those of q and dout, read once for both;
   // the dV role takes the k rows as queries and the carried state G as is,
   // the dK role the v rows and G transposed (q2 = v rows, o2 = dk)
-  kPsGradFused = 7
+  kPsGradFused = 7,
+  // one part of a sequence cut along the tokens: fp32 initial state formed
+  // from the sequence's S_0 and the K^T V sums of the parts before it; only
+  // the last part stores its final state (PrefillArgs part_*)
+  kPsPart = 8,
+  // as kPsPart, with the parts' K^T V sums formed in the same launch: each
+  // part but the last first sums K^T V over its own tokens and publishes it
+  // behind a flag; each part then adds the published sums of the parts
+  // before it, in part order (PrefillArgs part_flags, part_epoch)
+  kPsPartLB = 9
 };
+
+// Longest wait of a part for a flag of an earlier part: about one second of
+// the 100 MHz constant clock (s_memrealtime).  The earlier part has no wait
+// before it publishes, so a wait this long means it could not run; the
+// waiting part then poisons its state with NaN instead of spinning on.
+constexpr unsigned long long kPartWaitTicks = 100000000ull;
 
 // Round x / scale to the storage format of SM and return the stored value
 // times scale (exact for power-of-two scales).
@@ -351,6 +366,17 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int nblk = nfull + (last > 0 ? 1 : 0);
   constexpr bool REV = SM == kPsGradRev || SM == kPsGradRevPair || SM == kPsGradFused;
   constexpr bool FUSED = SM == kPsGradFused;
+  constexpr bool NARROW = SM == kPsBF16 || SM == kPsE4M3;
+  constexpr bool GRAD = SM >= kPsGrad && SM <= kPsGradFused;
+  constexpr bool PART_LB = SM == kPsPartLB;
+  constexpr bool PART = SM == kPsPart || PART_LB;
+  // a part's sequence and its place in it (PART), else the sequence itself
+  const int64_t pseq = PART ? bh / a.part_P : bh;
+  const int ppart = PART ? (int)(bh % a.part_P) : 0;
+  // one-launch parts: block 0's tiles and Q rows requested before the main
+  // loop (lb_issued); every block's K and V tiles held in LDS from before the
+  // main loop to its end, where they fit the staging ring (kv_res)
+  [[maybe_unused]] bool lb_issued = false, kv_res = false;
   // first token (memory order) of the block processed at step j, of length len
   auto blk_tok0 = [&](int j, int len) -> int64_t {
     if constexpr (REV)
@@ -385,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   };
   // narrow formats: stored value = code * scale
   float lp_sc = 1.f;
-  if constexpr (SM >= kPsBF16) {
+  if constexpr (NARROW) {
     if (a.lp_scale) lp_sc = a.lp_scale[bh];
   }
   const float lp_inv = 1.f / lp_sc;
@@ -400,7 +426,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
           S_acc[x][y][e] = bf16_bits_to_f32(((const u16 *)a.lp_state)[s_at(x, y, e)]) * lp_sc;
         else if constexpr (SM == kPsE4M3)
           S_acc[x][y][e] = __builtin_amdgcn_cvt_f32_fp8((int)((const uint8_t *)a.lp_state)[s_at(x, y, e)], 0) * lp_sc;
-        else if constexpr (SM >= kPsGrad)
+        else if constexpr (PART_LB)
+          S_acc[x][y][e] = 0.f;  // the part's own K^T V is summed first
+        else if constexpr (PART)
+          S_acc[x][y][e] = a.part_s0[(size_t)pseq * D * D + (s_at(x, y, e) - (size_t)bh * D * D)];
+        else if constexpr (GRAD)
           S_acc[x][y][e] = !g_in ? 0.f
                            : g_in_t ? g_in[(size_t)bh * D * D +
                                            (size_t)(j0 + (jb * P::BJT + y) * 16 + lr) * D +
@@ -409,6 +439,40 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         else
           S_acc[x][y][e] = a.state[s_at(x, y, e)];
       }
+
+  // A part of a sequence cut along the tokens starts from S_0 plus the K^T V
+  // sums of the parts before it, added in part order.  The lane's elements of
+  // UNR consecutive sums are loaded before any of them is added (the sums are
+  // independent loads), so the prologue pays one memory round trip per UNR
+  // sums rather than one per sum.
+  if constexpr (PART && !PART_LB) {
+    constexpr int NE = P::BIT * P::BJT * 4;
+    constexpr int UNR = NE <= 16 ? 8 : (NE <= 32 ? 4 : 2);
+    const int nsum = ppart * a.part_S;
+    for (int c0 = 0; c0 < nsum; c0 += UNR) {
+      float t[UNR][P::BIT][P::BJT][4];
+#pragma unroll
+      for (int i = 0; i < UNR; ++i) {
+        const int c = c0 + i < nsum ? c0 + i : nsum - 1;
+        const float *ps = a.part_sums + ((size_t)c * a.part_BH + (size_t)pseq) * D * D - (size_t)bh * D * D;
+#pragma unroll
+        for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+          for (int y = 0; y < P::BJT; ++y)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[i][x][y][e] = ps[s_at(x, y, e)];
+      }
+#pragma unroll
+      for (int i = 0; i < UNR; ++i)
+#pragma unroll
+        for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+          for (int y = 0; y < P::BJT; ++y)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c0 + i < nsum) S_acc[x][y][e] += t[i][x][y][e];
+    }
+  }
 
   // ---- phase A role: row tiles {rg, NT-1-rg} x value tiles [jc0, jc0 + NJC) ----
   const bool act = P::AWAVES == kWaves || wave < P::AWAVES;
@@ -849,6 +913,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
   };
 
+  // ---- a ring of block slots over both stages (one-launch parts): each
+  // stage holds kBlkMax / (16 NT) blocks; the ring has at most 64 / N_DMA
+  // slots so that every wait on the blocks in flight fits a vmcnt ----
+  constexpr int NSUB = kBlkMax / (16 * NT);
+  constexpr int RING = (2 * NSUB - 1) * P::N_DMA <= 63 ? 2 * NSUB : 63 / P::N_DMA + 1;
+  [[maybe_unused]] auto slot_k = [&](int sl) { return (sl / NSUB ? Ks1 : Ks0) + (sl % NSUB) * 16 * NT * D; };
+  [[maybe_unused]] auto slot_v = [&](int sl) { return (sl / NSUB ? Vs1 : Vs0) + (sl % NSUB) * 16 * NT * DV; };
+
   // ---- one block.  On entry the Q rows and direct loads of block jblk
   // (into Kc, Vc), then the output stores of block jblk-1, may be in flight;
   // the other stage (Kn, Vn) is free (its block's reads ended at the previous
@@ -880,7 +952,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 1, kc);
     }
     auto vm_slot = [&](int slot) __attribute__((always_inline)) {
-      if (nlen > 0) {
+      if (nlen > 0 && !(PART_LB && kv_res)) {
 #pragma unroll
         for (int m = slot * P::N_DMA / P::NSLOT; m < (slot + 1) * P::N_DMA / P::NSLOT; ++m) kv_issue(dma, m);
       }
@@ -938,7 +1010,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
 
     // the carry stored in the narrow format after every block (if asked)
-    if constexpr (SM >= kPsBF16) {
+    if constexpr (NARROW) {
       if (a.lp_round) {
 #pragma unroll
         for (int x = 0; x < P::BIT; ++x)
@@ -1093,10 +1165,237 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     write_state_copy();
   };
 
+  // ---- one-launch part (kPsPartLB): the part's start state ----
+  // Flags of this sequence and value slice: published[j] and done[j] of part
+  // j at pub[j * kPartMaxSplit] and done_f[j * kPartMaxSplit].  Every wait is
+  // for a part of a lower workgroup id (parts are numbered along the grid in
+  // order, for each slice), and a part publishes before it waits, so with
+  // workgroups dispatched in id order every awaited part runs.
+  // The sums and flags cross XCDs, whose L2 caches are not coherent with one
+  // another.  They are written and read with device-scope (sc1) accesses,
+  // which the L2 keeps coherent, rather than with acquire/release fences: a
+  // device-scope fence writes back or invalidates the whole L2 of the XCD,
+  // under the feet of the other workgroups streaming through it.  Order: a
+  // part's sum stores complete (vmcnt) before any lane stores its flag; a
+  // reader issues its sum loads only after its flag load has returned.
+  [[maybe_unused]] unsigned long long *pub = nullptr, *slab_f = nullptr, *done_f = nullptr;
+  auto flag_now = [&](const unsigned long long *f) __attribute__((always_inline)) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto wait_flag = [&](const unsigned long long *f) __attribute__((always_inline)) {
+    bool seen = flag_now(f) == a.part_epoch;
+    if (!seen) {
+      const unsigned long long t0 = wall_clock64();
+      do {
+        __builtin_amdgcn_s_sleep(1);
+        seen = flag_now(f) == a.part_epoch;
+      } while (!seen && wall_clock64() - t0 < kPartWaitTicks);
+    }
+    // later loads stay after the flag load (a compiler barrier; the flag's
+    // value has returned before the loop ends)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return seen;
+  };
+  auto set_flag = [&](unsigned long long *f, unsigned long long v) __attribute__((always_inline)) {
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // whether v holds in any thread of the workgroup, through a word of the
+  // state copy's LDS (every byte of LDS is taken; the copy is not in use
+  // where this is called: before the main loop and after it)
+  auto any_thread = [&](bool v) __attribute__((always_inline)) {
+    __attribute__((address_space(3))) int *w = (__attribute__((address_space(3))) int *)(size_t)lds_addr(SsT);
+    __syncthreads();
+    if (tid == 0) *w = 0;
+    __syncthreads();
+    if (v) *w = 1;
+    __syncthreads();
+    const bool r = *w != 0;
+    __syncthreads();
+    return r;
+  };
+  // Sums and start states are stored in the order of the lanes' accumulator
+  // fragments (part, sequence, slice: [wave][x][y][lane][4] floats), which
+  // every workgroup of the slice shares, so that a lane moves 16 contiguous
+  // bytes per access.  Steps of a part p (all parts of a sequence and slice
+  // run them side by side):
+  //  1. p < P-1: A_p = K^T V over its own tokens, published (flag pub[p]);
+  //  2. every part takes 1/P of the slice's elements and forms, for them,
+  //     the start of every part, start_{j+1} = start_j + A_j from start_0 =
+  //     S_0, in part order; published (flag slab[p]);
+  //  3. part p reads its own start (part 0: S_0) and sets done[p].
+  // The last part stores S_N over S_0, and clears the flags, once every
+  // other part is done.
+  if constexpr (PART_LB) {
+    const int np = a.part_P;
+    pub = a.part_flags + (size_t)pseq * np * kPartMaxSplit + split;
+    const size_t flag_stride = (size_t)a.part_BH * np * kPartMaxSplit;
+    slab_f = pub + flag_stride;
+    done_f = slab_f + flag_stride;
+    // Byte offsets in the sums (and the starts, which follow them): element
+    // (x, y) of this lane in region (j, seq, slice), and the region's base.
+    // A one-launch cut has P <= kPartMaxOneLaunch and B H P <= the
+    // compute-unit count, so both arrays span at most 2 (P - 1) B H d^2 4
+    // < 2^31 bytes.
+    const size_t region = (size_t)a.part_BH * D * D * 4;  // bytes from part j to j+1
+    const uint32_t base0 = (uint32_t)(((size_t)pseq * D * D + (size_t)split * D * DV) * 4);
+    const uint32_t lane0 = (uint32_t)(((size_t)wave * P::BIT * P::BJT * 256 + (size_t)lane_now() * 4) * 4);
+    auto frag_at = [&](int j, int x, int y) {
+      return base0 + lane0 + (uint32_t)((size_t)j * region + (size_t)(x * P::BJT + y) * 1024);
+    };
+    const uint32_t all_bytes = (uint32_t)(2 * (size_t)(np - 1) * region);
+    const uint32_t starts0 = (uint32_t)((size_t)(np - 1) * region);
+    const u32x4 dsum = raw_desc(a.part_sums_w, all_bytes);
+    __amdgpu_buffer_rsrc_t rs;
+    __builtin_memcpy(&rs, &dsum, sizeof(rs));
+    // cache policy 16: sc1, device-scope coherent
+    constexpr int kSc1 = 16;
+
+    kv_res = nblk <= RING;
+    if (ppart == np - 1 && kv_res) {
+      // the last part has no sum to form: its tiles are requested now, into
+      // the ring, and arrive while it waits for the other parts
+      for (int b = 0; b < nblk; ++b) kv_issue_all(kv_prepare((int64_t)b * blk, block_len(b), slot_k(b), slot_v(b)));
+    }
+    if (ppart < np - 1) {
+      // 1. K^T V over the part's own tokens (this slice's columns).  The
+      // blocks' K and V tiles are staged as in the main loop, in the ring of
+      // slots; where they all fit, they stay there for the main loop.
+      const LaneOff lop = lane_off();
+      int ktrP[P::BIT], vtrP[P::BJT];
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x) ktrP[x] = ktr(lop, ib * P::BIT + x);
+#pragma unroll
+      for (int y = 0; y < P::BJT; ++y) vtrP[y] = vtr(lop, jb * P::BJT + y);
+      int issued = 0;
+      for (; issued < nblk && issued < RING; ++issued)
+        kv_issue_all(kv_prepare((int64_t)issued * blk, block_len(issued), slot_k(issued), slot_v(issued)));
+      for (int pb = 0; pb < nblk; ++pb) {
+        const int sl = pb % RING;
+        const u16 *Kc = slot_k(sl);
+        const u16 *Vc = slot_v(sl);
+        wait_vmcnt((issued - pb - 1) * P::N_DMA);  // block pb has landed
+        lds_barrier();
+#pragma unroll
+        for (int cc = 0; cc < P::NCC; ++cc) {
+          const int c0 = 32 * cc;
+          bf16x8 ka[P::BIT], vb[P::BJT];
+#pragma unroll
+          for (int x = 0; x < P::BIT; ++x) ka[x] = ldtr(Kc, ktrP[x] + c0 * RB, ktrP[x] + (c0 + 16) * RB);
+#pragma unroll
+          for (int y = 0; y < P::BJT; ++y) vb[y] = ldtr(Vc, vtrP[y] + c0 * VRB, vtrP[y] + (c0 + 16) * VRB);
+#pragma unroll
+          for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+            for (int y = 0; y < P::BJT; ++y) S_acc[x][y] = mfma_16x16x32(ka[x], vb[y], S_acc[x][y]);
+        }
+        lds_barrier();  // every wave is done with this slot
+        if (issued < nblk) {
+          kv_issue_all(kv_prepare((int64_t)issued * blk, block_len(issued), slot_k(sl), slot_v(sl)));
+          ++issued;
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, S_acc[x][y]), rs, (int)frag_at(ppart, x, y), 0,
+                                                 kSc1);
+      wait_vmcnt(0);    // this wave's sum stores are complete
+      __syncthreads();  // ... and every other wave's
+      if (tid == 0) set_flag(pub + (size_t)ppart * kPartMaxSplit, a.part_epoch);
+    }
+    // the main loop's first tiles (unless held in the ring) and Q rows,
+    // requested now so that they arrive during steps 2 and 3
+    {
+      const int len0 = block_len(0);
+      if (!kv_res) kv_issue_all(kv_prepare(0, len0, Ks0, Vs0));
+      load_q(0, len0);
+      lb_issued = true;
+    }
+
+    // 2. the starts of every part for elements [ppart F, ppart F + F) of the
+    // region (in float4s).  A thread's P - 1 sums are loaded together.
+    bool ok = true;
+    for (int j = tid; j < np - 1; j += kThreads)
+      if (!wait_flag(pub + (size_t)j * kPartMaxSplit)) ok = false;
+    __syncthreads();  // every sum is published (or a wait ran out)
+    {
+      constexpr int E4 = D * DV / 4;
+      const int F = E4 / np;
+      for (int i = ppart * F + tid; i < (ppart + 1) * F; i += kThreads) {
+        // fragment position -> state element: i = ((w BIT + x) BJT + y) 64 + l
+        const int l = i & 63, t = i >> 6;
+        const int y = t % P::BJT, x = (t / P::BJT) % P::BIT, w = t / (P::BJT * P::BIT);
+        const int row = ((w % P::PBR) * P::BIT + x) * 16 + 4 * (l >> 4);
+        const int col = j0 + ((w / P::PBR) * P::BJT + y) * 16 + (l & 15);
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = a.state[(size_t)pseq * D * D + (size_t)(row + e) * D + col];
+        const uint32_t off = base0 + (uint32_t)i * 16;
+        constexpr int kMaxTerms = kPartMaxOneLaunch - 1;
+        f32x4 t4[kMaxTerms];
+#pragma unroll
+        for (int k = 0; k < kMaxTerms; ++k)
+          if (k < np - 1)
+            t4[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + k * region), 0, kSc1));
+#pragma unroll
+        for (int k = 0; k < kMaxTerms; ++k)
+          if (k < np - 1) {
+            acc += t4[k];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), rs,
+                                                   (int)(starts0 + off + k * region), 0, kSc1);
+          }
+      }
+    }
+    wait_vmcnt(0);  // this wave's start stores (and the tiles and Q rows above) are complete
+    __syncthreads();
+    if (tid == 0) set_flag(slab_f + (size_t)ppart * kPartMaxSplit, a.part_epoch);
+
+    // 3. this part's start: S_0 for part 0, else start_p from every slab
+    if (ppart == 0) {
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            S_acc[x][y][e] = a.state[s_at(x, y, e) - (size_t)bh * D * D + (size_t)pseq * D * D];
+    } else {
+      for (int q = tid; q < np; q += kThreads)
+        if (!wait_flag(slab_f + (size_t)q * kPartMaxSplit)) ok = false;
+      __syncthreads();  // every slab is published
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y)
+          S_acc[x][y] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(starts0 + frag_at(ppart - 1, x, y)), 0, kSc1));
+    }
+    // a wait that ran out (some part could not run): no valid start state
+    if (any_thread(!ok)) {
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y)
+          S_acc[x][y] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+    if (ppart < np - 1) {
+      // every wave has its start (the loads are consumed by the branch above)
+#pragma unroll
+      for (int x = 0; x < P::BIT; ++x)
+#pragma unroll
+        for (int y = 0; y < P::BJT; ++y) asm volatile("" ::"v"(S_acc[x][y]));
+      __syncthreads();
+      if (tid == 0) set_flag(done_f + (size_t)ppart * kPartMaxSplit, a.part_epoch);
+    }
+  }
+
   {
     const int len0 = block_len(0);
-    kv_issue_all(kv_prepare(REV ? blk_tok0(0, len0) : 0, len0, Ks0, Vs0));
-    load_q(REV ? blk_tok0(0, len0) : 0, len0);
+    if (!(PART_LB && lb_issued)) {
+      kv_issue_all(kv_prepare(REV ? blk_tok0(0, len0) : 0, len0, Ks0, Vs0));
+      load_q(REV ? blk_tok0(0, len0) : 0, len0);
+    }
     if constexpr (FUSED) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -1122,6 +1421,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     if constexpr (FUSED) {
       body_fused(jblk, Ks0, Vs0, Ks1, Vs1);
       if (jblk + 1 < nblk) body_fused(jblk + 1, Ks1, Vs1, Ks0, Vs0);
+    } else if (PART_LB && kv_res) {
+      // tiles held in the ring: no direct loads in the loop
+      body(jblk, slot_k(jblk % RING), slot_v(jblk % RING), Ks0, Vs0);
+      if (jblk + 1 < nblk) body(jblk + 1, slot_k((jblk + 1) % RING), slot_v((jblk + 1) % RING), Ks0, Vs0);
     } else {
       body(jblk, Ks0, Vs0, Ks1, Vs1);
       if (jblk + 1 < nblk) body(jblk + 1, Ks1, Vs1, Ks0, Vs0);
@@ -1129,11 +1432,22 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   }
 
   // ---- final state ----
+  // The last part of a one-launch cut stores S_N over S_0 only once every
+  // other part of its slice has read S_0 (done flags).
+  [[maybe_unused]] bool lb_done = true;
+  if constexpr (PART_LB) {
+    if (ppart == a.part_P - 1) {
+      bool mine = true;
+      for (int j = tid; j < a.part_P - 1; j += kThreads)
+        if (!wait_flag(done_f + (size_t)j * kPartMaxSplit)) mine = false;
+      lb_done = !any_thread(!mine);
+    }
+  }
   // Nothing of this wave may still be in flight when it ends: a gradient pass
   // may have no block to process, and then the first block's direct loads
   // into LDS were never awaited.  (Forward passes always have a block, whose
   // loads the loop awaits.)
-  if constexpr (SM >= kPsGrad) wait_vmcnt(0);
+  if constexpr (GRAD) wait_vmcnt(0);
 #pragma unroll
   for (int x = 0; x < P::BIT; ++x)
 #pragma unroll
@@ -1148,13 +1462,29 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         for (int e = 0; e < 4; ++e) {
           if constexpr (SM == kPsBF16)
             ((u16 *)a.lp_state)[s_at(x, y, e)] = f32_to_bf16_bits(S_acc[x][y][e] * lp_inv);
-          else if constexpr (SM >= kPsGrad) {
+          else if constexpr (GRAD) {
             if (g_out) g_out[s_at(x, y, e)] = S_acc[x][y][e];
+          } else if constexpr (PART) {
+            if (ppart == a.part_P - 1) a.state[(size_t)pseq * D * D + (s_at(x, y, e) - (size_t)bh * D * D)] = S_acc[x][y][e];
           } else
             a.state[s_at(x, y, e)] = S_acc[x][y][e];
         }
       }
     }
+  // The last part of a one-launch cut then clears the flags of the other
+  // parts (each is done with the flags and sums it reads), so that the next
+  // call (or graph replay, with the same epoch) starts from zero.
+  if constexpr (PART_LB) {
+    if (ppart == a.part_P - 1 && lb_done) {
+      for (int j = tid; j < a.part_P; j += kThreads) {
+        if (j < a.part_P - 1) {
+          set_flag(pub + (size_t)j * kPartMaxSplit, 0ull);
+          set_flag(done_f + (size_t)j * kPartMaxSplit, 0ull);
+        }
+        set_flag(slab_f + (size_t)j * kPartMaxSplit, 0ull);
+      }
+    }
+  }
 }
 
 template <int D, int DV, int SM>
@@ -1171,8 +1501,9 @@ hipError_t launch_nt(const PrefillArgs &a, int64_t BH, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Launch over the (d, nsplit) variants; sets the XCD mapping.
-template <int SM>
+// Launch over the (d, nsplit) variants; sets the XCD mapping.  (D64: whether
+// the d = 64 variants exist.)
+template <int SM, bool D64 = true>
 hipError_t prefill_bf16_dispatch(PrefillArgs a, int64_t BH, int d, hipStream_t stream) {
   a.xcd_map = (a.nsplit > 1 && (BH * a.nsplit) % (8 * a.nsplit) == 0) ? 1 : 0;
   if (d == 128) {
@@ -1182,9 +1513,11 @@ hipError_t prefill_bf16_dispatch(PrefillArgs a, int64_t BH, int d, hipStream_t s
       case 4: return launch_nt<128, 32, SM>(a, BH, stream);
     }
   } else if (d == 64) {
-    switch (a.nsplit) {
-      case 1: return launch_nt<64, 64, SM>(a, BH, stream);
-      case 2: return launch_nt<64, 32, SM>(a, BH, stream);
+    if constexpr (D64) {
+      switch (a.nsplit) {
+        case 1: return launch_nt<64, 64, SM>(a, BH, stream);
+        case 2: return launch_nt<64, 32, SM>(a, BH, stream);
+      }
     }
   }
   return hipErrorInvalidValue;

@@ -377,6 +377,13 @@ __global__ __launch_bounds__(kThreadsSD) void state_split_bf16_kernel(StateSplit
     for (int y = 0; y < NJW; ++y)
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[(size_t)(16 * x + 4 * g + e) * D + 16 * (NJW * wave + y) + lr] = acc[x][y][e];
+  // the sequence's initial state, copied for the parts of a prefill cut along
+  // the tokens (the final state will be written over it)
+  if (a.all_partial && a.s0_copy && c == 0) {
+    const f32x4 *src = (const f32x4 *)(a.state + (size_t)bh * D * D);
+    f32x4 *dst = (f32x4 *)(a.s0_copy + (size_t)bh * D * D);
+    for (int i = threadIdx.x; i < D * D / 4; i += kThreadsSD) dst[i] = src[i];
+  }
 }
 
 // state += the partial sums of chunks 1 .. chunks-1, in chunk order; 4 values
@@ -390,25 +397,6 @@ __global__ __launch_bounds__(256) void state_split_reduce_kernel(StateSplitArgs 
   f32x4 acc = *st;
   for (int64_t c = 1; c < a.chunks; ++c) acc += ((const f32x4 *)(a.partial + ((size_t)(c - 1) * a.BH + bh) * D * D))[i];
   *st = acc;
-}
-
-__global__ __launch_bounds__(256) void part_starts_kernel(const float *state, const float *partial, float *starts,
-                                                         int64_t BH, int64_t P, int64_t S, int64_t per_head4) {
-  const int64_t bh = blockIdx.x / (per_head4 / 256);
-  const int64_t i = (int64_t)(blockIdx.x % (per_head4 / 256)) * 256 + threadIdx.x;  // float4 index
-  f32x4 acc = ((const f32x4 *)state)[bh * per_head4 + i];
-  ((f32x4 *)starts)[(bh * P) * per_head4 + i] = acc;
-  for (int64_t p = 1; p < P; ++p) {
-    for (int64_t c = (p - 1) * S; c < p * S; ++c) acc += ((const f32x4 *)partial)[(c * BH + bh) * per_head4 + i];
-    ((f32x4 *)starts)[(bh * P + p) * per_head4 + i] = acc;
-  }
-}
-
-__global__ __launch_bounds__(256) void take_last_kernel(const float *starts, float *state, int64_t P,
-                                                       int64_t per_head4) {
-  const int64_t bh = blockIdx.x / (per_head4 / 256);
-  const int64_t i = (int64_t)(blockIdx.x % (per_head4 / 256)) * 256 + threadIdx.x;
-  ((f32x4 *)state)[bh * per_head4 + i] = ((const f32x4 *)starts)[(bh * P + P - 1) * per_head4 + i];
 }
 
 template <int D>
@@ -448,22 +436,6 @@ hipError_t state_split_launch(StateSplitArgs a, int d, hipStream_t stream) {
   if (d == 128) return launch_split<128>(a, stream);
   if (d == 64) return launch_split<64>(a, stream);
   return hipErrorInvalidValue;
-}
-
-hipError_t state_part_starts_launch(const float *state, const float *partial, float *starts, int64_t BH,
-                                    int64_t P, int64_t S, int d, hipStream_t stream) {
-  const int64_t per_head4 = (int64_t)d * d / 4;  // 4096 or 1024: a multiple of 256
-  hipLaunchKernelGGL(part_starts_kernel, dim3((unsigned)(BH * (per_head4 / 256))), dim3(256), 0, stream, state,
-                     partial, starts, BH, P, S, per_head4);
-  return hipGetLastError();
-}
-
-hipError_t state_take_last_launch(const float *starts, float *state, int64_t BH, int64_t P, int d,
-                                  hipStream_t stream) {
-  const int64_t per_head4 = (int64_t)d * d / 4;
-  hipLaunchKernelGGL(take_last_kernel, dim3((unsigned)(BH * (per_head4 / 256))), dim3(256), 0, stream, starts, state,
-                     P, per_head4);
-  return hipGetLastError();
 }
 
 void state_split_plan(int64_t BH, int64_t N, int cus, int64_t *chunks, int64_t *chunk_len) {

@@ -353,7 +353,7 @@ def test_seqsplit_noalloc_validation():
     """The scratch-buffer variant rejects what the workspace variant rejects,
     and reports its fixed buffer size; it needs no workspace arguments."""
     lib = la.library()
-    assert lib.lin_attn_scratch_bytes() == 64 << 20
+    assert lib.lin_attn_scratch_bytes() == 56 << 20
     f = lib.lin_attn_prefill_seqsplit_noalloc
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 96, 128, la.BF16, None) == la.EUNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 8192, 128, 100, la.BF16, None) == la.EUNSUPPORTED

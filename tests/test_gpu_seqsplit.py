@@ -2,9 +2,12 @@
 against the fp64 oracle.
 
 Each sequence's tokens are cut into P parts; the parts' initial states come
-from the K^T V of the parts before them (the token-split accumulation plus an
-ordered prefix sum), and the parts run as independent chunked prefills.  The
-outputs and the final state are those of the whole sequence.
+from the K^T V of the parts before them, added in part order, and the parts
+run as independent chunked prefills.  At d = 128, up to 32 parts per
+sequence form those starts in the same launch (each part publishes its own
+K^T V behind a flag, then the parts form the starts together); otherwise a
+separate token-split state pass runs first.  The outputs and the final state are those of
+the whole sequence.
 
 Gates as for the prefill: max|gpu - oracle| / max|oracle| <= 1e-2 (bf16
 inputs, fp32 state); exact for exact-integer inputs.
@@ -34,12 +37,15 @@ def gpu_seqsplit(q, k, v, S0, block, dtype="bf16", workspace=None):
 
 
 @pytest.mark.parametrize("B,H,N,d,block", [
-    (1, 4, 16384, 128, 128),   # 32 parts of 512
-    (2, 2, 8192, 64, 64),      # 16 parts
-    (1, 1, 4176, 128, 128),    # 8 parts of 522: ragged last block in every part
-    (1, 3, 12288, 128, 64),    # 16 parts of 768
-    (1, 1, 65536, 128, 128),   # 64 parts of 1024, 1 accumulation chunk each
-    (1, 2, 16384, 64, 128),    # 32 parts of 512 (d = 64)
+    (1, 4, 16384, 128, 128),   # 64 parts of 256: two launches
+    (2, 2, 8192, 64, 64),      # 32 parts of 256: two launches (d = 64)
+    (1, 1, 4176, 128, 128),    # 16 parts of 261: one launch, ragged last block in every part
+    (1, 3, 12288, 128, 64),    # 32 parts of 384: one launch, 3 sequences
+    (1, 1, 65536, 128, 128),   # 256 parts of 256: two launches, 1 state-pass chunk each
+    (1, 2, 16384, 64, 128),    # 64 parts of 256 (d = 64): two launches
+    (1, 32, 32768, 64, 64),    # 8 parts of 4096: two launches, 4 state-pass chunks per part
+    (1, 32, 32768, 128, 128),  # 8 parts of 4096: one launch, 32 blocks per part
+    (1, 4, 20480, 128, 128),   # 64 parts of 320: two launches, ragged last block in every part
 ])
 def test_seqsplit_random(B, H, N, d, block):
     ws = la.prefill_seqsplit_workspace(B, H, N, d, block, torch.bfloat16)
@@ -78,9 +84,9 @@ def test_seqsplit_uncut_cases_and_workspace():
     the plain prefill, bitwise; a workspace one byte short is rejected; a
     cut call is bitwise repeatable."""
     announce("prefill seqsplit uncut / workspace / determinism")
-    q, k, v = synth.prefill_inputs(42, 2, 2, 1000, 128)  # 1000 tokens: no cut (parts of 500 < 512)
+    q, k, v = synth.prefill_inputs(42, 2, 2, 500, 128)  # 500 tokens: no cut (parts of 250 < 256)
     S0 = random_state(3, (2, 2), 128)
-    assert la.prefill_seqsplit_workspace(2, 2, 1000, 128, 128, torch.bfloat16) == 0
+    assert la.prefill_seqsplit_workspace(2, 2, 500, 128, 128, torch.bfloat16) == 0
     o, S = gpu_seqsplit(q, k, v, S0, 128)
     o1, S1 = gpu_prefill(q, k, v, S0, 128, "bf16")
     np.testing.assert_array_equal(o, o1)  # no cut: the plain prefill, bitwise
@@ -99,6 +105,48 @@ def test_seqsplit_uncut_cases_and_workspace():
     Sd = torch.zeros((B, H, d, d), device="cuda")
     with pytest.raises(la.LinAttnError):
         la.prefill_seqsplit(qd, kd, vd, od, Sd, 128, torch.empty(need - 1, dtype=torch.uint8, device="cuda"))
+
+
+def test_seqsplit_one_launch_workspace_contents_do_not_matter():
+    """A one-launch cut (B=1 H=8 N=4096 d=128 block 64: 16 parts of 256
+    tokens) gives the same result, bitwise, from a zeroed workspace, from one
+    full of random bytes and from the workspace a previous call left; each
+    call leaves the flag words it used zero (those of parts 0 .. P-2 in the
+    value slices its parts run in; the last part has no flag)."""
+    B, H, N, d, blk = 1, 8, 4096, 128, 64
+    P = 16
+    sums = (P - 1) * B * H * d * d * 4
+    need = la.prefill_seqsplit_workspace(B, H, N, d, blk, torch.bfloat16)
+    announce("prefill seqsplit one launch, workspace contents", B, H, N, d, blk, f"workspace {need}")
+    assert need == 2 * sums + B * H * P * 3 * 4 * 8
+    q, k, v = synth.prefill_inputs_device(44, B, H, N, d)
+    S0 = torch.from_numpy(random_state(44, (B, H), d)).cuda()
+    g = torch.Generator(device="cuda").manual_seed(44)
+    workspaces = [torch.zeros(need, dtype=torch.uint8, device="cuda"),
+                  torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=g)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nsplit = 1
+    while nsplit < 4 and B * H * P * nsplit < cus:
+        nsplit *= 2
+    results = []
+    for ws in workspaces + [workspaces[1]]:
+        o, S = torch.empty_like(q), S0.clone()
+        la.prefill_seqsplit(q, k, v, o, S, blk, ws)
+        torch.cuda.synchronize()
+        flags = ws[2 * sums:].view(torch.int64).view(3, B * H, P, 4)  # published, slab, done
+        used = torch.cat([flags[0, :, :P - 1, :nsplit].flatten(), flags[1, :, :, :nsplit].flatten(),
+                          flags[2, :, :P - 1, :nsplit].flatten()])
+        assert not torch.any(used), f"flag words left set: {torch.nonzero(flags).tolist()[:8]}"
+        results.append((o, S))
+    for o, S in results[1:]:
+        assert torch.equal(o, results[0][0]) and torch.equal(S, results[0][1])
+    o_u, S_u = torch.empty_like(q), S0.clone()
+    la.prefill(q, k, v, o_u, S_u, blk)
+    torch.cuda.synchronize()
+    d_o = (results[0][0].float() - o_u.float()).abs().max().item() / o_u.float().abs().max().item()
+    d_s = (results[0][1] - S_u).abs().max().item() / S_u.abs().max().item()
+    print(f"  cut vs uncut prefill: o {d_o:.3e} state {d_s:.3e}", flush=True)
+    assert d_o <= TOL_BF16 and d_s <= 1e-4
 
 
 def test_seqsplit_shard_workload_sampled():
@@ -146,10 +194,15 @@ def test_workspace_queries_on_this_device():
     assert q(4, 64, 32768, 128, la.BF16) == 0                         # 256 sequences: one chunk each
     assert q(1, 2, 255, 128, la.BF16) == 0                            # too short to split
     p = lib.lin_attn_prefill_seqsplit_workspace
-    # 64 sequences of 131072 tokens: 4 parts of 32768, 4 accumulation chunks each:
-    # 3 * 4 * 64 partial states + 64 * 4 part states, 64 KiB each
-    assert p(1, 64, 131072, 128, 128, la.BF16) == (3 * 4 * 64 + 64 * 4) * 128 * 128 * 4
+    # 64 sequences of 131072 tokens: 4 parts of 32768, one launch: 3 * 64 part
+    # sums and 3 * 64 start states of 64 KiB, then three flag arrays of
+    # 64 * 4 * 4 words of 8 bytes
+    assert p(1, 64, 131072, 128, 128, la.BF16) == 2 * 3 * 64 * 128 * 128 * 4 + 3 * 64 * 4 * 4 * 8
+    # 4 sequences of 16384 tokens: 64 parts of 256, two launches (one state-pass
+    # chunk each): 63 * 4 partial states + a copy of the 4 initial states
+    assert p(1, 4, 16384, 128, 128, la.BF16) == (63 * 4 + 4) * 128 * 128 * 4
     assert p(4, 64, 32768, 128, 128, la.BF16) == 0
     assert p(1, 8, 4095, 128, 128, la.BF16) == 0       # indivisible: no cut
-    # 8 sequences of 8192 tokens: 16 parts of 512, one chunk each
-    assert p(1, 8, 8192, 128, 128, la.BF16) == (15 * 8 + 8 * 16) * 128 * 128 * 4
+    # 8 sequences of 8192 tokens: 32 parts of 256, one launch
+    assert p(1, 8, 8192, 128, 128, la.BF16) == 2 * 31 * 8 * 128 * 128 * 4 + 3 * 8 * 32 * 4 * 8
+    assert p(1, 8, 510, 128, 128, la.BF16) == 0        # parts of 255 < 256: no cut

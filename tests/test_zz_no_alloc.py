@@ -43,9 +43,14 @@ def run_both(B, H, N, d, block, seed):
 
 
 def test_noalloc_matches_workspace_entry_point_on_consecutive_calls():
-    # largest first: the C4 shard (64 sequences x 131072 tokens, 4 parts of 4
-    # accumulation chunks: a 64 MiB plan), then smaller calls over its leftovers
-    cases = [(1, 64, 131072, 128, 128, 61), (1, 8, 8192, 128, 128, 62), (1, 2, 4096, 64, 64, 63)]
+    # largest plan first, then smaller ones over its leftovers in the buffer:
+    #  - one sequence of 2^19 tokens: 256 parts of 2048, two launches (state
+    #    pass in 2 chunks per part): 511 states, 31.9 MiB;
+    #  - the 1M-token sequence's shard (64 sequences x 131072 tokens, 4 parts,
+    #    one launch): 24 MiB;
+    #  - 8 sequences x 8192 tokens (32 parts, one launch) and 2 x 4096 at d = 64
+    cases = [(1, 1, 1 << 19, 128, 128, 60), (1, 64, 131072, 128, 128, 61), (1, 8, 8192, 128, 128, 62),
+             (1, 2, 4096, 64, 64, 63)]
     for i, (B, H, N, d, block, seed) in enumerate(cases):
         inputs, (o_ws, S_ws), (o_sc, S_sc) = run_both(B, H, N, d, block, seed)
         assert torch.equal(o_sc, o_ws), f"call {i}: outputs differ from the workspace entry point"
@@ -76,7 +81,7 @@ def test_noalloc_uncut_case_needs_no_scratch():
 def test_noalloc_refuses_a_plan_larger_than_the_scratch():
     """One sequence of 2^21 tokens at d = 128 is cut into as many parts as
     the GPU has compute units, each summed in 4 chunks: on a 256-unit device
-    that plan needs 79.75 MiB, more than the 64 MiB buffer; the call returns
+    that plan needs 63.8 MiB, more than the 56 MiB buffer; the call returns
     LIN_ATTN_ESCRATCH before any launch and leaves its outputs untouched."""
     B, H, N, d, block = 1, 1, 1 << 21, 128, 128
     need = la.prefill_seqsplit_workspace(B, H, N, d, block, torch.bfloat16)
