@@ -20,7 +20,8 @@ work.  Every kernel is timed with HIP events on the stream it runs on;
 heads) over the timed steps.  Prints ONE JSON line.
 
 ``--only crossover`` sweeps the chunked and the token-by-token prefill over
-N = 256 ... 32768 at the crossover shape (see crossover_sweep).
+N = 256 ... 32768 at the crossover shape (see crossover_sweep); the default
+run includes the sweep at 5 launches a point (``crossover_sweep``).
 ``--only long`` times the long-context prefill (B=1, H=64, N=1048576, d=128,
 block 128; 16 GiB per tensor) with the value-column split and with the
 sequence split (see long_context).
@@ -705,6 +706,8 @@ def main():
     torch.cuda.empty_cache()
     long_res = long_context(la, synth, torch, keep_sample=not args.no_cpu_baseline)
     long_res, long_sample = long_res if isinstance(long_res, tuple) else (long_res, None)
+    # the crossover sweep over sequence length (8 and 256 heads), 5 launches a point
+    sweep = crossover_sweep(la, synth, torch, steps=5)
     p_bytes = prefill_bytes(**P)
     p_flops = prefill_flops(**P)
     p_dense = prefill_dense_flops(**P)
@@ -828,6 +831,7 @@ def main():
             "frac_of_same_mix_stream_reference": gbs / max(ceiling["r3w1_GBps"], ceiling["r3w1_roles_GBps"]),
         },
         "long": long_res,
+        "crossover_sweep": sweep,
         "hbm_stream_reference": ceiling,
         "timing": {"wall_ms_timed_region": wall_ms, "setup_s": setup_s,
                    "method": "HIP events on the launch stream around each kernel"},
@@ -856,7 +860,7 @@ def crossover_sweep(la, synth, torch, steps: int = 20):
     write that evicts the last-level cache; times are HIP-event averages
     over `steps` launches.  The chunked form runs as lin_attn_prefill and as
     lin_attn_prefill_seqsplit (which cuts the sequences into parts of at
-    least 512 tokens to fill the GPU).  A modeled line gives causal softmax attention at
+    least 256 tokens to fill the GPU).  A modeled line gives causal softmax attention at
     the bf16 matrix peak, 2 N^2 d flop per head (not built; context only).
     """
     B, d, blk = CROSSOVER["B"], CROSSOVER["d"], CROSSOVER["block"]
