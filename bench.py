@@ -642,6 +642,17 @@ def main():
             timed("prefill_snapshots", lambda: la.prefill_snapshots(pq, pk, pv, po, pS2, psnap, P["block"],
                                                                     SNAP_EVERY))
             timed("backward", lambda: la.backward(pq, pk, pv, pdo, pdq, pdk, pdv, P["block"], dstate0=pdS0))
+        # The shard's kernels run right after the 32K-token passes, and the
+        # decode group after them: the speculative verify, a read-only pass
+        # over 1 GiB of states, measured 15 % slower (same clock, same
+        # requests, a higher L2 read latency) whenever the decode group
+        # followed the 32K-token passes or the crossover trio, and not after
+        # the shard's kernels or at the start of a step.
+        if need["shard"]:
+            timed("shard_state_accumulate", lambda: la.state_accumulate_split(hk, hv, hdS, hws))
+            timed("shard_state_accumulate_tiles", lambda: la.state_accumulate(hk, hv, hdS2))
+            timed("shard_prefill", lambda: la.prefill(hq, hk, hv, ho, hS0, SH["block"]))
+            timed("shard_prefill_seqsplit", lambda: la.prefill_seqsplit(hq, hk, hv, ho2, hS0b, SH["block"], hpws))
         if need["decode"]:
             if last:
                 keep("decode_S", dS32)
@@ -665,11 +676,6 @@ def main():
             timed("small_recurrent", lambda: la.prefill_recurrent(sq, sk, sv, so2, sS2))
             flush.fill_(0)
             timed("small_chunked_seqsplit", lambda: la.prefill_seqsplit(sq, sk, sv, so3, sS3, S["block"], sws))
-        if need["shard"]:
-            timed("shard_state_accumulate", lambda: la.state_accumulate_split(hk, hv, hdS, hws))
-            timed("shard_state_accumulate_tiles", lambda: la.state_accumulate(hk, hv, hdS2))
-            timed("shard_prefill", lambda: la.prefill(hq, hk, hv, ho, hS0, SH["block"]))
-            timed("shard_prefill_seqsplit", lambda: la.prefill_seqsplit(hq, hk, hv, ho2, hS0b, SH["block"], hpws))
 
     for _ in range(args.warmup):
         step(None)
