@@ -352,7 +352,9 @@ int lin_attn_state_accumulate_split(const void *k, const void *v, float *state,
  *    random 64-bit value when set; a wait longer than about one second
  *    (only possible when the parts of a launch cannot all run, e.g. a device
  *    shared with a kernel that never yields) gives NaN outputs instead of
- *    hanging.
+ *    hanging.  The environment variable LIN_ATTN_PART_WAIT_TICKS, read at
+ *    each call, sets that bound in ticks of the 100 MHz constant clock (a
+ *    test setting: 0 makes waits run out).
  *  - otherwise two launches.  The token-split accumulation sums the K^T V of
  *    the first P-1 parts into the workspace (which also receives a copy of
  *    S_0); the parts then run as B*H*P prefills, each adding the sums of the

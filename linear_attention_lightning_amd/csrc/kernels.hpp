@@ -63,9 +63,16 @@ struct PrefillArgs {
   float *part_sums_w;
   unsigned long long *part_flags;
   unsigned long long part_epoch;
+  unsigned long long part_wait_ticks;  // bound of each wait, in 100 MHz clock ticks
 };
 constexpr int kPartMaxSplit = 4;
 constexpr int kPartMaxOneLaunch = 32;
+// Longest wait of a part for a flag of another part (PrefillArgs
+// part_wait_ticks), by default: about one second of the 100 MHz constant
+// clock (s_memrealtime).  Every awaited part reaches its flag without waiting
+// on the waiter, so a wait this long means it could not run; the waiting part
+// then poisons what it produces with NaN instead of spinning on.
+constexpr unsigned long long kPartWaitTicks = 100000000ull;
 // Two reversed gradient passes of the same BH sequences in one launch: pass
 // 1 from the q, k, v, o, g_* pointers, pass 2 from the *2 pointers.  The
 // two passes must read the same key and value tensors (k2, v2 = v, k); the

@@ -5,6 +5,7 @@
 // call, so invalid arguments never reach the device.
 #include <atomic>
 #include <chrono>
+#include <cstdlib>
 #include <random>
 
 #include "kernels.hpp"
@@ -565,6 +566,20 @@ uint64_t next_part_epoch() {
   return z;
 }
 
+// Bound of each wait between the parts of a one-launch cut, in ticks of the
+// 100 MHz constant clock: about one second, or LIN_ATTN_PART_WAIT_TICKS from
+// the environment (a test setting: a small bound makes waits run out and
+// their parts' results NaN, which shows that every wait ends).
+uint64_t part_wait_ticks() {
+  const char *ev = getenv("LIN_ATTN_PART_WAIT_TICKS");
+  if (ev && *ev) {
+    char *end = nullptr;
+    const unsigned long long v = strtoull(ev, &end, 10);
+    if (end && *end == 0) return v;
+  }
+  return lal::kPartWaitTicks;
+}
+
 // The launches of a prefill cut along the tokens (plan pl, P > 1), with the
 // workspace at `workspace` (pl.ws_bytes bytes).
 // One-launch plan: the parts as B*H*P sequences of L tokens, each part but
@@ -603,6 +618,7 @@ int seqsplit_run(const SeqSplitPlan &pl, const void *q, const void *k, const voi
     a.part_sums_w = partial;
     a.part_flags = (unsigned long long *)(partial + 2 * (size_t)(pl.P - 1) * pl.BH * d * d);
     a.part_epoch = next_part_epoch();
+    a.part_wait_ticks = part_wait_ticks();
     return from_hip(lal::prefill_bf16_part_lb_launch(a, parts, (int)d, s));
   }
   float *s0_copy = partial + (size_t)(pl.P - 1) * pl.S * pl.BH * d * d;

@@ -115,11 +115,6 @@ enum PrefillStateMode {
   kPsPartLB = 9
 };
 
-// Longest wait of a part for a flag of an earlier part: about one second of
-// the 100 MHz constant clock (s_memrealtime).  The earlier part has no wait
-// before it publishes, so a wait this long means it could not run; the
-// waiting part then poisons its state with NaN instead of spinning on.
-constexpr unsigned long long kPartWaitTicks = 100000000ull;
 
 // Round x / scale to the storage format of SM and return the stored value
 // times scale (exact for power-of-two scales).
@@ -1189,7 +1184,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       do {
         __builtin_amdgcn_s_sleep(1);
         seen = flag_now(f) == a.part_epoch;
-      } while (!seen && wall_clock64() - t0 < kPartWaitTicks);
+      } while (!seen && wall_clock64() - t0 < a.part_wait_ticks);
     }
     // later loads stay after the flag load (a compiler barrier; the flag's
     // value has returned before the loop ends)
@@ -1318,7 +1313,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     bool ok = true;
     for (int j = tid; j < np - 1; j += kThreads)
       if (!wait_flag(pub + (size_t)j * kPartMaxSplit)) ok = false;
-    __syncthreads();  // every sum is published (or a wait ran out)
+    // every sum is published, or some wait ran out: then the slab's starts are
+    // NaN, so that no part starts from sums that were never written
+    const bool sums_ok = !any_thread(!ok);
     {
       constexpr int E4 = D * DV / 4;
       const int F = E4 / np;
@@ -1338,6 +1335,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         for (int k = 0; k < kMaxTerms; ++k)
           if (k < np - 1)
             t4[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + k * region), 0, kSc1));
+        if (!sums_ok) acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
 #pragma unroll
         for (int k = 0; k < kMaxTerms; ++k)
           if (k < np - 1) {

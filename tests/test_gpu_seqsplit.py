@@ -46,6 +46,8 @@ def gpu_seqsplit(q, k, v, S0, block, dtype="bf16", workspace=None):
     (1, 32, 32768, 64, 64),    # 8 parts of 4096: two launches, 4 state-pass chunks per part
     (1, 32, 32768, 128, 128),  # 8 parts of 4096: one launch, 32 blocks per part
     (1, 4, 20480, 128, 128),   # 64 parts of 320: two launches, ragged last block in every part
+    (2, 64, 1024, 128, 128),   # 2 parts of 512: one launch, the smallest cut
+    (1, 8, 4096, 128, 32),     # 16 parts of 256, block 32: one launch, 8 blocks held in the staging ring
 ])
 def test_seqsplit_random(B, H, N, d, block):
     ws = la.prefill_seqsplit_workspace(B, H, N, d, block, torch.bfloat16)
@@ -147,6 +149,49 @@ def test_seqsplit_one_launch_workspace_contents_do_not_matter():
     d_s = (results[0][1] - S_u).abs().max().item() / S_u.abs().max().item()
     print(f"  cut vs uncut prefill: o {d_o:.3e} state {d_s:.3e}", flush=True)
     assert d_o <= TOL_BF16 and d_s <= 1e-4
+
+
+def test_seqsplit_one_launch_waits_always_end():
+    """The waits between the parts of a one-launch cut are bounded.  With the
+    bound forced to zero ticks (LIN_ATTN_PART_WAIT_TICKS, which the library
+    reads at each call), waits run out: the call still ends, and parts whose
+    waits ran out give NaN rather than results from sums never written.  The
+    next call, with the normal bound and the same workspace, is bitwise the
+    normal result and leaves its flag words zero."""
+    import os
+    B, H, N, d, blk = 1, 8, 4096, 128, 64
+    P = 16
+    need = la.prefill_seqsplit_workspace(B, H, N, d, blk, torch.bfloat16)
+    announce("prefill seqsplit one launch, zero-tick waits", B, H, N, d, blk)
+    q, k, v = synth.prefill_inputs_device(45, B, H, N, d)
+    S0 = torch.from_numpy(random_state(45, (B, H), d)).cuda()
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    o_ref, S_ref = torch.empty_like(q), S0.clone()
+    la.prefill_seqsplit(q, k, v, o_ref, S_ref, blk, ws)
+    torch.cuda.synchronize()
+    os.environ["LIN_ATTN_PART_WAIT_TICKS"] = "0"
+    try:
+        o, S = torch.empty_like(q), S0.clone()
+        la.prefill_seqsplit(q, k, v, o, S, blk, ws)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["LIN_ATTN_PART_WAIT_TICKS"]
+    n_nan = int(torch.isnan(o.float()).sum())
+    print(f"  zero-tick waits: {n_nan} of {o.numel()} outputs NaN", flush=True)
+    assert n_nan > 0, "no wait ran out"
+    o2, S2 = torch.empty_like(q), S0.clone()
+    la.prefill_seqsplit(q, k, v, o2, S2, blk, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o_ref) and torch.equal(S2, S_ref)
+    sums = (P - 1) * B * H * d * d * 4
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nsplit = 1
+    while nsplit < 4 and B * H * P * nsplit < cus:
+        nsplit *= 2
+    flags = ws[2 * sums:].view(torch.int64).view(3, B * H, P, 4)
+    used = torch.cat([flags[0, :, :P - 1, :nsplit].flatten(), flags[1, :, :, :nsplit].flatten(),
+                      flags[2, :, :P - 1, :nsplit].flatten()])
+    assert not torch.any(used), "flag words left set"
 
 
 def test_seqsplit_shard_workload_sampled():
