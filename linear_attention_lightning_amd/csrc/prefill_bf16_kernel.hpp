@@ -323,6 +323,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   __shared__ __attribute__((aligned(1024))) u16 Vs0[kBlkMax * DV];
   __shared__ __attribute__((aligned(1024))) u16 Vs1[kBlkMax * DV];
   __shared__ __attribute__((aligned(1024))) u16 SsT[DV * D];  // SsT[j][i] = bf16(S[i][j0 + j])
+  // One-launch parts with at most 64 value columns leave 48 KiB of LDS free:
+  // there the Q rows of blocks 1 .. nblk-1 of a short part are staged
+  // (QSLOT blocks), laid out and swizzled as K tiles.
+  constexpr bool QLDS = SM == kPsPartLB && DV <= 64;
+  constexpr int kQsElems = QLDS ? 48 * 1024 / 2 : 8;
+  constexpr int QSLOT = QLDS ? kQsElems / (16 * NT * D) : 0;
+  __shared__ __attribute__((aligned(1024))) u16 Qs[kQsElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -370,8 +377,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
   const int ppart = PART ? (int)(bh % a.part_P) : 0;
   // one-launch parts: block 0's tiles and Q rows requested before the main
   // loop (lb_issued); every block's K and V tiles held in LDS from before the
-  // main loop to its end, where they fit the staging ring (kv_res)
-  [[maybe_unused]] bool lb_issued = false, kv_res = false;
+  // main loop to its end, where they fit the staging ring (kv_res); the Q
+  // rows of blocks 1 .. nblk-1 staged in LDS before the main loop too, where
+  // they fit its Q slots (q_res)
+  [[maybe_unused]] bool lb_issued = false, kv_res = false, q_res = false;
   // first token (memory order) of the block processed at step j, of length len
   auto blk_tok0 = [&](int j, int len) -> int64_t {
     if constexpr (REV)
@@ -657,6 +666,20 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
     for (int m = 0; m < P::N_DMA; ++m) kv_issue(d, m);
   };
+  // Q rows of block b >= 1 into its LDS slot (one-launch parts, QLDS), by
+  // the K tiles' direct loads
+  [[maybe_unused]] auto q_slot = [&](int b) { return Qs + (b - 1) * 16 * NT * D; };
+  [[maybe_unused]] auto q_issue = [&](int64_t tok0, int len, u16 *Qd) __attribute__((always_inline)) {
+    unsigned zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+#pragma unroll
+    for (int m = 0; m < P::KI_W; ++m) {
+      const int inst = wave + kWaves * m;
+      const int step = m * kWaves * P::KRPI * RB;
+      const u32x4 desc = raw_desc(qh + (size_t)tok0 * D, inst < P::KINST ? (uint32_t)len * D * 2 + zero : 0u);
+      dma_b128(desc, kv_lk + step, lds_addr(Qd) + inst * 1024);
+    }
+  };
   auto block_len = [&](int jb) { return jb < nfull ? blk : last; };
 
 
@@ -932,7 +955,19 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // Wait for this block's tiles and Q rows; the previous block's 2 NJC
     // output stores, issued after them, may stay in flight.
     wait_vmcnt(jblk == 0 ? 0 : P::NST);
-    take_q();
+    if (PART_LB && q_res && jblk > 0) {
+      // Q rows from their LDS slot, in the fragment order of the K rows
+      // (filled before the main loop; block 0's wait and barrier made them
+      // visible)
+      const LaneOff lq = lane_off();
+      const u16 *Qc = q_slot(jblk);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kc = 0; kc < P::NKC; ++kc) bq[u][kc] = ld128(Qc, kfrag(lq, kc) + 16 * (u ? T1 : T0) * RB);
+    } else {
+      take_q();
+    }
     lds_barrier();  // every wave's tiles of block jblk and the state copy are in LDS
 
     // the next block's loads, one share per issue slot
@@ -941,10 +976,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     // inside the per-row-tile branches of phase A, their destination registers
     // differ between branches, and the compiler's wait analysis, which merges
     // the branches, then drains all loads in flight at the start of phase A.
+    if (!(PART_LB && q_res)) {
 #pragma unroll
-    for (int kc = 0; kc < P::NKC; ++kc) {
-      load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 0, kc);
-      load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 1, kc);
+      for (int kc = 0; kc < P::NKC; ++kc) {
+        load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 0, kc);
+        load_q_part(REV ? blk_tok0(jblk + 1, nlen) : tok0 + blk, nlen, 1, kc);
+      }
     }
     auto vm_slot = [&](int slot) __attribute__((always_inline)) {
       if (nlen > 0 && !(PART_LB && kv_res)) {
@@ -1300,11 +1337,17 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
       if (tid == 0) set_flag(pub + (size_t)ppart * kPartMaxSplit, a.part_epoch);
     }
     // the main loop's first tiles (unless held in the ring) and Q rows,
-    // requested now so that they arrive during steps 2 and 3
+    // requested now so that they arrive during steps 2 and 3; the later
+    // blocks' Q rows too, where they fit the Q slots
     {
       const int len0 = block_len(0);
       if (!kv_res) kv_issue_all(kv_prepare(0, len0, Ks0, Vs0));
       load_q(0, len0);
+      if constexpr (QLDS) {
+        q_res = kv_res && nblk - 1 <= QSLOT;
+        if (q_res)
+          for (int b = 1; b < nblk; ++b) q_issue((int64_t)b * blk, block_len(b), q_slot(b));
+      }
       lb_issued = true;
     }
 
