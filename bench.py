@@ -31,9 +31,10 @@ default run includes it).
 ``--only ceiling`` measures the HBM bandwidth a plain streaming kernel
 reaches for the path's read:write byte mixes (see hbm_stream_reference); the default
 run includes it.
-``--only drift`` instead measures the rounding drift of stored states against
-the fp64 oracle along one 1M-token sequence (not part of a step; see
-drift_report).
+``--only drift`` measures the rounding drift of stored states against the
+fp64 oracle along one 1M-token sequence (not part of a step; see
+drift_report); the default run includes it with the oracle timings
+(``drift``; left out with --no-cpu-baseline).
 """
 from __future__ import annotations
 
@@ -486,7 +487,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg: its timing, the error check and the drift report")
     ap.add_argument("--only", choices=["prefill", "decode", "recurrent", "shard", "copy", "drift", "crossover",
                                        "ceiling", "long", "decode128"],
                     help="run one kernel only (for counter collection); prints timings, no JSON")
@@ -849,6 +850,9 @@ def main():
             (dq, dk, dv, last_in["decode_S"], last_in["decode_o"], last_in["decode_SN"]),
             long_sample)
         out["error_vs_oracle"]["gates"] = {"bf16_io_fp32_state": 1e-2, "fp32_io": 1e-4}
+        # the oracle leg also gives the stored-state drift along one 1M-token
+        # sequence (about 25 s, with its own progress lines on stderr)
+        out["drift"] = drift_report(la, synth, torch)
     print(json.dumps(out))
 
 

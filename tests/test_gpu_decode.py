@@ -125,6 +125,7 @@ def test_decode_after_prefill():
                                         (1, 2, 130, 128, "fp32"), (1, 1, 1, 64, "fp32"),
                                         # 8-column slices (B*H*d/8 >= 256 > B*H*d/16 on 256 compute units)
                                         (1, 16, 100, 128, "bf16"), (1, 32, 50, 64, "fp32"),
+                                        (1, 16, 90, 128, "fp32"), (1, 32, 61, 64, "bf16"),
                                         # enough sequences for the 16-column slices (B*H*d/16 >= 256)
                                         (2, 16, 200, 128, "bf16"), (4, 16, 45, 64, "fp32"),
                                         (2, 16, 70, 128, "fp32"), (4, 16, 45, 64, "bf16")])
