@@ -179,7 +179,7 @@ def cpu_baseline(prefill, small, decode, long_sample, reps: int = 3):
             ts.append(time.perf_counter() - t0)
         return sorted(ts)[len(ts) // 2], out
 
-    configs, errors = {}, {}
+    per_workload, errors = {}, {}
     # prefill and crossover workloads: the token-by-token fp64 recurrence
     for name, (tensors, H_all) in (("prefill_B4_H64_N32768", (prefill, 64)),
                                    ("crossover_B1_H8_N4096", (small, 8))):
@@ -188,7 +188,7 @@ def cpu_baseline(prefill, small, decode, long_sample, reps: int = 3):
         S0 = S_in.double().cpu().numpy()
         dt, (o_ref, S_ref) = timed(lambda: oracle.recurrence(qh, kh, vh, S0, nthreads=threads))
         heads, N, d = qh.shape[-3], qh.shape[-2], qh.shape[-1]
-        configs[name] = {"seconds_median": dt, "heads": heads, "tokens_per_head": N,
+        per_workload[name] = {"seconds_median": dt, "heads": heads, "tokens_per_head": N,
                          "head_tokens_per_s": heads * N / dt,
                          "tokens_per_s": heads * N / dt / H_all,
                          "gflops_fp64": heads * N * 4 * d * d / dt / 1e9}
@@ -208,7 +208,7 @@ def cpu_baseline(prefill, small, decode, long_sample, reps: int = 3):
 
     dt, o_ref = timed(one_step)
     nseq = qh.shape[0] * qh.shape[1]
-    configs["decode_256x64_d128"] = {"seconds_median": dt, "sequences": nseq, "tokens_per_s": qh.shape[0] / dt,
+    per_workload["decode_256x64_d128"] = {"seconds_median": dt, "sequences": nseq, "tokens_per_s": qh.shape[0] / dt,
                                      "state_GBps_fp64": nseq * 2 * 128 * 128 * 8 / dt / 1e9}
     errors["decode_256x64_d128"] = {"o": _rel_err(_host(o_gpu), o_ref),
                                     "state": _rel_err(S_gpu.cpu().numpy(), state["S"])}
@@ -219,7 +219,7 @@ def cpu_baseline(prefill, small, decode, long_sample, reps: int = 3):
         o_ref, S_ref = oracle.recurrence(qh, kh, vh, nthreads=threads)
         dt = time.perf_counter() - t0
         N = qh.shape[-2]
-        configs["long_B1_H64_N1048576"] = {
+        per_workload["long_B1_H64_N1048576"] = {
             "seconds_4_heads": dt, "heads": len(LONG_HEADS), "runs": 1,
             "extrapolated_seconds_64_heads": dt / -(-len(LONG_HEADS) // threads) * -(-64 // threads),
             "extrapolation": "extrapolated, not measured: the oracle runs one head per thread, so 64 heads take "
@@ -235,7 +235,7 @@ def cpu_baseline(prefill, small, decode, long_sample, reps: int = 3):
             cpu_model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), "")
     except OSError:
         pass
-    head = configs["prefill_B4_H64_N32768"]
+    head = per_workload["prefill_B4_H64_N32768"]
     baseline = {
         "value": head["tokens_per_s"],
         "unit": "tokens/s",
@@ -246,7 +246,7 @@ def cpu_baseline(prefill, small, decode, long_sample, reps: int = 3):
         "sample": f"prefill workload batch entry 0 (64 of the 256 sequences, N=32768, d=128), the GPU's own "
                   f"inputs and initial states, fp64 token-by-token recurrence, median of {reps} runs "
                   f"({head['seconds_median']:.2f} s each, {head['gflops_fp64']:.1f} GFLOP/s fp64)",
-        "configs": configs,
+        "configs": per_workload,
     }
     return baseline, errors
 
