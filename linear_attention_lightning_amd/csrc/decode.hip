@@ -7,7 +7,9 @@
 // memory.  It moves 2 d^2 state elements per 4 d^2 flop, so the kernel is a
 // streaming read-modify-write of the state at HBM speed:
 //
-//  * one wavefront per (batch, head); four per 256-thread workgroup;
+//  * one or two wavefronts per (batch, head), four per 256-thread
+//    workgroup; two split a head's rows and add their partial outputs in
+//    wave order through LDS;
 //  * each lane owns 16 bytes of a state row (4 fp32, 8 bf16 or 16 fp8
 //    columns) and walks the rows that map to it, so every state access is a
 //    coalesced, non-temporal 16-byte load or store;
@@ -40,116 +42,152 @@ __device__ __forceinline__ float load_io(const void *p, size_t i) {
     return ((const float *)p)[i];
 }
 
-template <int D, bool IO_BF16, int ST>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void decode_kernel(DecodeArgs a) {
-  constexpr int ES = ST == kStF32 ? 4 : ST == kStBF16 ? 2 : 1;  // bytes per state element
-  constexpr int VE = 16 / ES;          // state elements per 16-byte access
-  constexpr int LPR = D / VE;          // lanes covering one state row
-  constexpr int RP = 64 / LPR;         // rows covered by one wave access
-  constexpr int RPL = D / RP;          // rows per lane
-  // rows in flight per lane: 16 for bf16 states (4-6 % faster than 8); 8 for
-  // fp32 (16 measured no faster) and E4M3 (16, its whole share in one batch,
-  // measured 4 % slower)
-  constexpr int UMAX = ST == kStBF16 ? 16 : 8;
-  constexpr int U = RPL < UMAX ? RPL : UMAX;
-  static_assert(RPL % U == 0, "row unroll");
+// Shape of the state walk for d = D and the storage format ST: each lane
+// moves 16 bytes of a state row per access.
+template <int D, int ST>
+struct DecodeShape {
+  static constexpr int ES = ST == kStF32 ? 4 : ST == kStBF16 ? 2 : 1;  // bytes per state element
+  static constexpr int VE = 16 / ES;   // state elements per 16-byte access
+  static constexpr int LPR = D / VE;   // lanes covering one state row
+  static constexpr int RP = 64 / LPR;  // rows covered by one wave access
+  static constexpr int RPL = D / RP;   // row steps of one head
+};
 
-  __shared__ float2 qk[kWavesPerBlock][D];
+// Waves per head (WPH), rows per lane in one batch of loads (U), and whether
+// the next batch's loads are issued before the current batch is updated
+// (PIPE).  Measured at 256 x 64 sequences, d = 128, bf16 I/O, against the
+// earlier choice of one wave per head and unpipelined batches (16 rows for
+// bf16 states, 8 otherwise); the stored states are bitwise the same:
+//  * fp32 state: 2 waves per head, pipelined batches of 4 rows: 0.347 ms
+//    against 0.379 ms.  One wave with pipelined batches of 4, 8 or 16 rows:
+//    0.375-0.381 ms; 4 waves per head: 0.364-0.376 ms.
+//  * bf16 state: 1 wave per head, pipelined batches of 8 rows: 0.178 ms
+//    against 0.183 ms; 2 waves per head: 0.181-0.186 ms.
+//  * E4M3 state: 2 waves per head, each with its 8 rows in one batch:
+//    0.0875 ms against 0.091 ms; pipelined batches of 4: 0.088 ms.
+template <int D, int ST>
+struct DecodeTune {
+  static constexpr int WPH = ST == kStBF16 ? 1 : 2;
+  static constexpr int UMAX = ST == kStF32 ? 4 : 8;
+  static constexpr bool PIPE = ST != kStE4M3;
+};
+
+template <int D, bool IO_BF16, int ST, int WPH, int U, bool PIPE>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void decode_kernel(DecodeArgs a) {
+  using Sh_ = DecodeShape<D, ST>;
+  constexpr int VE = Sh_::VE, LPR = Sh_::LPR, RP = Sh_::RP, RPL = Sh_::RPL;
+  constexpr int HPB = kWavesPerBlock / WPH;  // heads per workgroup
+  constexpr int RW = RPL / WPH;              // row steps per wave
+  static_assert(kWavesPerBlock % WPH == 0 && RPL % WPH == 0 && RW % U == 0, "row split");
+
+  __shared__ float2 qk[HPB][D];
+  __shared__ float red[WPH > 1 ? kWavesPerBlock : 1][WPH > 1 ? VE : 1][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int64_t h = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const int hl = wave / WPH, sub = wave % WPH;  // head within the workgroup, part of its rows
+  const int64_t h = (int64_t)blockIdx.x * HPB + hl;
   const bool valid = h < a.BH;
   // stored units: S' = S / scale (fp32 states are never scaled)
   const float sc = (ST != kStF32 && valid && a.scale) ? a.scale[h] : 1.f;
   const float inv = 1.f / sc;
 
-  if (valid) {
+  if (valid && sub == 0) {
     for (int i = lane; i < D; i += 64)
-      qk[wave][i] = make_float2(load_io<IO_BF16>(a.q, (size_t)h * D + i) * sc,
-                                load_io<IO_BF16>(a.k, (size_t)h * D + i));
+      qk[hl][i] = make_float2(load_io<IO_BF16>(a.q, (size_t)h * D + i) * sc,
+                              load_io<IO_BF16>(a.k, (size_t)h * D + i));
   }
   __syncthreads();
-  if (!valid) return;
 
   const int cg = lane % LPR;  // column group: columns cg*VE .. cg*VE+VE-1
   const int rph = lane / LPR; // rows rph, rph+RP, ...
   float vj[VE], acc[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) {
-    vj[e] = load_io<IO_BF16>(a.v, (size_t)h * D + cg * VE + e) * inv;
+    vj[e] = valid ? load_io<IO_BF16>(a.v, (size_t)h * D + cg * VE + e) * inv : 0.f;
     acc[e] = 0.f;
   }
 
-  u32x4 *Sh = (u32x4 *)((char *)a.state + (size_t)h * D * D * ES);  // 16-byte units
-  constexpr int U16_PER_ROW = D * ES / 16;
+  u32x4 *Sh = (u32x4 *)((char *)a.state + (size_t)h * D * D * Sh_::ES);  // 16-byte units
+  constexpr int U16_PER_ROW = D * Sh_::ES / 16;
+  const int m_lo = sub * RW;  // this wave's row steps: m_lo .. m_lo + RW - 1
+  auto row_at = [&](int m) { return Sh + (size_t)(rph + RP * m) * U16_PER_ROW + cg; };
+  // S_i += k_i v, o += q_i S_i for row step m, then the row is stored back
+  auto update = [&](int m, const u32x4 &raw) __attribute__((always_inline)) {
+    const float2 qki = qk[hl][rph + RP * m];
+    u32x4 w;
+    if constexpr (ST == kStE4M3) {
+      // each 32-bit word holds four fp8 state entries (byte 0 first)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        f32x4 sv = e4m3x4_to_f32(raw[x]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = fmaf(qki.y, vj[4 * x + e], sv[e]);
+          acc[4 * x + e] = fmaf(qki.x, sv[e], acc[4 * x + e]);
+        }
+        w[x] = f32_to_e4m3x4(sv);
+      }
+    } else if constexpr (ST == kStBF16) {
+      // each 32-bit word holds two bf16 state entries (low half first)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t word = raw[x];
+        float s0 = __uint_as_float(word << 16);
+        float s1 = __uint_as_float(word & 0xffff0000u);
+        s0 = fmaf(qki.y, vj[2 * x], s0);
+        s1 = fmaf(qki.y, vj[2 * x + 1], s1);
+        acc[2 * x] = fmaf(qki.x, s0, acc[2 * x]);
+        acc[2 * x + 1] = fmaf(qki.x, s1, acc[2 * x + 1]);
+        const bf16x2 packed = {(bf16)s0, (bf16)s1};
+        w[x] = __builtin_bit_cast(uint32_t, packed);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float se = fmaf(qki.y, vj[e], __uint_as_float(raw[e]));
+        acc[e] = fmaf(qki.x, se, acc[e]);
+        w[e] = __float_as_uint(se);
+      }
+    }
+    __builtin_nontemporal_store(w, row_at(m));
+  };
 
-  if constexpr (ST == kStE4M3) {
-    // one batch of U rows per lane, the loop kept rolled: this form measured
-    // 5 % faster than the loop over both batches written out
-    auto rows = [&](int m0) {
-      u32x4 raw[U];
+  if (valid) {
+    if constexpr (PIPE) {
+      // the loads of batch b + 1 are in flight while batch b is updated
+      u32x4 cur[U], nxt[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = rph + RP * (m0 + u);
-        raw[u] = __builtin_nontemporal_load(Sh + (size_t)i * U16_PER_ROW + cg);
-      }
+      for (int u = 0; u < U; ++u) cur[u] = __builtin_nontemporal_load(row_at(m_lo + u));
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = rph + RP * (m0 + u);
-        const float2 qki = qk[wave][i];
-        u32x4 w;
-        // each 32-bit word holds four fp8 state entries (byte 0 first)
+      for (int m0 = 0; m0 < RW; m0 += U) {
+        if (m0 + U < RW) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          f32x4 sv = e4m3x4_to_f32(raw[u][x]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[e] = fmaf(qki.y, vj[4 * x + e], sv[e]);
-            acc[4 * x + e] = fmaf(qki.x, sv[e], acc[4 * x + e]);
-          }
-          w[x] = f32_to_e4m3x4(sv);
+          for (int u = 0; u < U; ++u) nxt[u] = __builtin_nontemporal_load(row_at(m_lo + m0 + U + u));
         }
-        __builtin_nontemporal_store(w, Sh + (size_t)i * U16_PER_ROW + cg);
+#pragma unroll
+        for (int u = 0; u < U; ++u) update(m_lo + m0 + u, cur[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
       }
-    };
+    } else if constexpr (ST == kStE4M3) {
+      // batches of U rows, the loop kept rolled: this form measured 5 %
+      // faster than the loop over both batches written out
+      auto rows = [&](int m0) {
+        u32x4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(row_at(m_lo + m0 + u));
+#pragma unroll
+        for (int u = 0; u < U; ++u) update(m_lo + m0 + u, raw[u]);
+      };
 #pragma unroll 1
-    for (int m0 = 0; m0 < RPL; m0 += U) rows(m0);
-  } else {
-    for (int m0 = 0; m0 < RPL; m0 += U) {
-      u32x4 raw[U];
+      for (int m0 = 0; m0 < RW; m0 += U) rows(m0);
+    } else {
+      for (int m0 = 0; m0 < RW; m0 += U) {
+        u32x4 raw[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = rph + RP * (m0 + u);
-        raw[u] = __builtin_nontemporal_load(Sh + (size_t)i * U16_PER_ROW + cg);
-      }
+        for (int u = 0; u < U; ++u) raw[u] = __builtin_nontemporal_load(row_at(m_lo + m0 + u));
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = rph + RP * (m0 + u);
-        const float2 qki = qk[wave][i];
-        u32x4 w;
-        if constexpr (ST == kStBF16) {
-          // each 32-bit word holds two bf16 state entries (low half first)
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const uint32_t word = raw[u][x];
-            float s0 = __uint_as_float(word << 16);
-            float s1 = __uint_as_float(word & 0xffff0000u);
-            s0 = fmaf(qki.y, vj[2 * x], s0);
-            s1 = fmaf(qki.y, vj[2 * x + 1], s1);
-            acc[2 * x] = fmaf(qki.x, s0, acc[2 * x]);
-            acc[2 * x + 1] = fmaf(qki.x, s1, acc[2 * x + 1]);
-            const bf16x2 packed = {(bf16)s0, (bf16)s1};
-            w[x] = __builtin_bit_cast(uint32_t, packed);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float se = fmaf(qki.y, vj[e], __uint_as_float(raw[u][e]));
-            acc[e] = fmaf(qki.x, se, acc[e]);
-            w[e] = __float_as_uint(se);
-          }
-        }
-        __builtin_nontemporal_store(w, Sh + (size_t)i * U16_PER_ROW + cg);
+        for (int u = 0; u < U; ++u) update(m_lo + m0 + u, raw[u]);
       }
     }
   }
@@ -159,8 +197,20 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void decode_kernel(DecodeArgs 
   for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
     for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  // the waves of one head add their sums in wave order
+  if constexpr (WPH > 1) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) red[wave][e][lane] = acc[e];
+    __syncthreads();
+    if (sub == 0) {
+#pragma unroll
+      for (int s = 1; s < WPH; ++s)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] += red[wave + s][e][lane];
+    }
+  }
 
-  if (rph == 0) {
+  if (valid && sub == 0 && rph == 0) {
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       const size_t oi = (size_t)h * D + cg * VE + e;
@@ -174,9 +224,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void decode_kernel(DecodeArgs 
 
 template <int D, bool IO, int ST>
 hipError_t go(const DecodeArgs &a, hipStream_t stream) {
-  const int64_t grid = (a.BH + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((decode_kernel<D, IO, ST>), dim3((unsigned)grid), dim3(64 * kWavesPerBlock), 0,
-                     stream, a);
+  using T = DecodeTune<D, ST>;
+  constexpr int RW = DecodeShape<D, ST>::RPL / T::WPH;
+  constexpr int U = RW < T::UMAX ? RW : T::UMAX;
+  constexpr int HPB = kWavesPerBlock / T::WPH;
+  const int64_t grid = (a.BH + HPB - 1) / HPB;
+  hipLaunchKernelGGL((decode_kernel<D, IO, ST, T::WPH, U, T::PIPE>), dim3((unsigned)grid),
+                     dim3(64 * kWavesPerBlock), 0, stream, a);
   return hipGetLastError();
 }
 
