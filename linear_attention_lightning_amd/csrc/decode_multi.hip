@@ -99,14 +99,14 @@ constexpr size_t verify_lds_bytes() {
 //
 // WPH waves share a head: each walks RPL / WPH of its row steps and the
 // second adds its state part to the first's through LDS.
-template <int D, bool IO_BF16, int ST, int TM, int WPH>
+template <int D, bool IO_BF16, int ST, int TM, int WPH, int UV = 8, bool PIPE = false>
 __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   constexpr int ES = ST == kStF32 ? 4 : ST == kStBF16 ? 2 : 1;
   constexpr int LPR = D / 4;    // lanes per state row (4 columns each)
   constexpr int RP = 64 / LPR;  // rows per wave access
   constexpr int RPL = D / RP;   // rows per lane
   constexpr int RW = RPL / WPH;  // row steps per wave
-  constexpr int U = RW < 8 ? RW : 8;  // rows in flight per lane
+  constexpr int U = RW < UV ? RW : UV;  // rows per lane in one batch of loads
   constexpr int HPB = kWV / WPH;     // heads per workgroup
   static_assert(kWV % WPH == 0 && RPL % WPH == 0 && RW % U == 0, "row split");
   static_assert(TM % 4 == 0, "LDS rows of whole float4s");
@@ -218,11 +218,26 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
     }
   };
   if (valid) {
+    if constexpr (PIPE) {
+      // the loads of batch b + 1 are in flight while batch b is multiplied
+      float cur[U][4], nxt[U][4];
+      load_rows(cur, sub * RW);
+#pragma unroll
+      for (int m0 = sub * RW; m0 < (sub + 1) * RW; m0 += U) {
+        if (m0 + U < (sub + 1) * RW) load_rows(nxt, m0 + U);
+        mult_rows(cur, m0);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cur[u][e] = nxt[u][e];
+      }
+    } else {
 #pragma unroll 1
-    for (int m0 = sub * RW; m0 < (sub + 1) * RW; m0 += U) {
-      float s[U][4];
-      load_rows(s, m0);
-      mult_rows(s, m0);
+      for (int m0 = sub * RW; m0 < (sub + 1) * RW; m0 += U) {
+        float s[U][4];
+        load_rows(s, m0);
+        mult_rows(s, m0);
+      }
     }
   }
   // lanes with equal cg hold partial sums over disjoint rows
@@ -497,17 +512,21 @@ void commit_kernel(DecodeMultiArgs a) {
 //  * commit, bf16 state: 2 waves, pipelined 4-row batches: 0.154 ms against
 //    0.160 (one wave pipelined 8 rows: 0.159);
 //  * commit, E4M3 state: 2 waves, one batch of 8 rows: 0.080 ms against 0.086;
-//  * verify: 2 waves: 0.180 ms against 0.183 (fp32 state), 0.096 against
-//    0.097 (bf16 state).
+//  * verify: 2 waves, and for an fp32 state with room for 4 drafts pipelined
+//    16-row batches: 0.175 ms against 0.184 (unpipelined 8 rows: 0.181;
+//    pipelined 8 rows: 0.178); bf16 state, unpipelined 8 rows: 0.097 ms
+//    against 0.098 (pipelined 8 or 16 rows: 0.098, 0.103).
 template <int ST>
 struct CommitTune {
   static constexpr int WPH = 2;
   static constexpr int UMAX = ST == kStE4M3 ? 8 : 4;
   static constexpr bool PIPE = ST != kStE4M3;
 };
-template <int ST>
+template <int ST, int TM>
 struct VerifyTune {
   static constexpr int WPH = 2;
+  static constexpr bool PIPE = ST == kStF32 && TM <= 4;  // registers for two batches
+  static constexpr int UV = PIPE ? 16 : 8;
 };
 
 template <int D, bool IO, int ST, int TM>
@@ -524,12 +543,13 @@ void commit_go(const DecodeMultiArgs &a, hipStream_t stream) {
 
 template <int D, bool IO, int ST, int TM>
 void verify_go(const DecodeMultiArgs &a, hipStream_t stream) {
-  constexpr int WPH = VerifyTune<ST>::WPH;
-  constexpr int HPB = kWV / WPH;
+  using V = VerifyTune<ST, TM>;
+  constexpr int HPB = kWV / V::WPH;
   const int64_t grid = (a.BH + HPB - 1) / HPB;
   // LDS scales with TM: 26 KiB at d = 128, bf16 I/O and TM = 16
   const size_t lds = (size_t)kWV * verify_lds_bytes<D, TM, IO>();
-  hipLaunchKernelGGL((verify_kernel<D, IO, ST, TM, WPH>), dim3((unsigned)grid), dim3(64 * kWV), lds, stream, a);
+  hipLaunchKernelGGL((verify_kernel<D, IO, ST, TM, V::WPH, V::UV, V::PIPE>), dim3((unsigned)grid), dim3(64 * kWV), lds,
+                     stream, a);
 }
 
 template <int D, bool IO, int ST>
