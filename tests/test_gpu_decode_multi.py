@@ -132,3 +132,26 @@ def test_verify_then_commit_matches_decode_outputs():
     la.decode_commit(dev(k, "bf16"), dev(v, "bf16"), Sd)
     torch.cuda.synchronize()
     assert torch.equal(Sd, S2)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_commit_odd_head_count_equals_decode_steps(d):
+    """Seven sequences with an fp32 state: the commit's last workgroup holds
+    one head and a pair of idle waves; its state is still bit-identical to
+    the accepted drafts' decode steps."""
+    announce("decode commit odd head count", d)
+    B, H, T = 7, 1, 5
+    q, k, v = drafts(61, B, H, T, d, "bf16")
+    S0 = random_state(12, (B, H), d, scale=2.0)
+    accept = np.array([5, 0, 3, 1, 4, 2, 5], dtype=np.int32)
+    Sd = torch.from_numpy(S0).cuda()
+    la.decode_commit(dev(k, "bf16"), dev(v, "bf16"), Sd, torch.from_numpy(accept).cuda())
+    Sb = torch.from_numpy(S0).cuda()
+    for b in range(B):
+        od = torch.empty((1, H, d), dtype=torch.bfloat16, device="cuda")
+        Sv = Sb[b:b + 1]
+        for t in range(int(accept[b])):
+            la.decode(dev(q[b:b + 1, :, t], "bf16"), dev(k[b:b + 1, :, t], "bf16"), dev(v[b:b + 1, :, t], "bf16"),
+                      od, Sv)
+    torch.cuda.synchronize()
+    assert torch.equal(Sd, Sb)

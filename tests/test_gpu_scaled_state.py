@@ -393,3 +393,36 @@ def test_commit_fp8_exact_integers():
     got = oracle.stored_to_f64(to_host_codes(Sd, "e4m3"), oracle.FMT_E4M3)
     for b in range(B):
         np.testing.assert_array_equal(got[b], oracle.state_after(k[b, :, :accept[b]], v[b, :, :accept[b]], S[b]))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "bf16"])
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_and_commit_odd_head_count(fmt, d):
+    """Seven sequences: decode and commit give two waves to each head (two
+    heads per workgroup), so the last workgroup holds one head and a pair of
+    idle waves.  Stored codes against the oracle's rounding, as above."""
+    announce("decode / commit odd head count", fmt, d)
+    B, H, T = 1, 7, 3
+    scale = scales_for((B, H), "pow2")
+    codes = decode_case(40, B, H, d, "bf16", fmt, scale)
+    scd = torch.from_numpy(scale).cuda()
+    # one decode step
+    Sd = to_device_codes(codes, fmt)
+    q, k, v = synth.decode_step_inputs(9, B, H, d, "bf16")
+    S_in = oracle.stored_to_f64(codes, FMTS[fmt], scale)
+    o_ref, S_exact = oracle.recurrence(q[:, :, None], k[:, :, None], v[:, :, None], S_in)
+    od = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
+    la.decode(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), od, Sd, state_scale=scd)
+    torch.cuda.synchronize()
+    check_codes(to_host_codes(Sd, fmt), S_exact, fmt, scale, rel_tol=2.0 ** -22)
+    assert rel_err(host(od), o_ref[:, :, 0]) <= TOL_IO["bf16"]
+    # a commit of all T drafts on the same codes
+    Sc = to_device_codes(codes, fmt)
+    _, kc, vc = synth.prefill_inputs(91, B, H, T, d, "bf16")
+    la.decode_commit(dev(kc, "bf16"), dev(vc, "bf16"), Sc, state_scale=scd)
+    torch.cuda.synchronize()
+    got = to_host_codes(Sc, fmt)
+    for h in range(H):
+        S_h = oracle.state_after(kc[0, h], vc[0, h], S_in[0, h])
+        check_codes(got[0, h], S_h, fmt, scale[0, h], rel_tol=2.0 ** -19,
+                    abs_tol=1e-6 * float(np.max(np.abs(S_h / scale[0, h]))))
