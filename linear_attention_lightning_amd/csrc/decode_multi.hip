@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
   float *qT = (float *)wl;                                     // qT[i * TM + t]
   KT *kT = (KT *)(wl + 4 * (size_t)D * TM);                    // kT[i * TM + t]
   float *P = (float *)(wl + (4 + sizeof(KT)) * (size_t)D * TM);  // P[t * TM + s] = q_t . k_s
-  __shared__ float red[WPH > 1 ? TM * 4 : 1][LPR];  // the second wave's state part
+  __shared__ float red[WPH > 1 ? HPB : 1][WPH > 1 ? TM * 4 : 1][LPR];  // each head's second wave's state part
   const int sub = wave % WPH;
   const int64_t h = (int64_t)blockIdx.x * HPB + wave / WPH;
   const bool valid = h < a.BH;
@@ -254,14 +254,14 @@ __global__ __launch_bounds__(64 * kWV) void verify_kernel(DecodeMultiArgs a) {
 #pragma unroll
       for (int t = 0; t < TM; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[4 * t + e][cg] = acc[t][e];
+        for (int e = 0; e < 4; ++e) red[wave / WPH][4 * t + e][cg] = acc[t][e];
     }
     __syncthreads();
     if (sub != 0) return;
 #pragma unroll
     for (int t = 0; t < TM; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] += red[4 * t + e][cg];
+      for (int e = 0; e < 4; ++e) acc[t][e] += red[wave / WPH][4 * t + e][cg];
   }
   if (!valid) return;
 
