@@ -30,6 +30,8 @@ def drafts(seed, B, H, T, d, dtype):
     (2, 2, 16, 64, "fp32"), (1, 3, 5, 128, "fp32"),
     # draft counts below the room of their variant (4, 8, 16), both I/O types
     (2, 3, 13, 128, "fp32"), (2, 5, 9, 128, "bf16"), (1, 3, 12, 64, "bf16"), (3, 3, 6, 128, "fp32"),
+    # room for 4 drafts at d = 64 (one pipelined batch per wave)
+    (2, 3, 3, 64, "bf16"), (1, 5, 4, 64, "fp32"),
 ])
 def test_verify_matches_oracle_and_leaves_state(B, H, T, d, io):
     announce("decode verify", B, H, T, d, io)
