@@ -797,6 +797,9 @@ def main():
         "crossover": {
             "chunked_ms": avg["small_chunked"], "recurrent_ms": avg["small_recurrent"],
             "chunked_seqsplit_ms": avg["small_chunked_seqsplit"],
+            "chunked_seqsplit_ms_median": sorted(kern_ms["small_chunked_seqsplit"])[len(kern_ms["small_chunked_seqsplit"]) // 2],
+            "chunked_seqsplit_ms_min": best["small_chunked_seqsplit"],
+            "recurrent_ms_median": sorted(kern_ms["small_recurrent"])[len(kern_ms["small_recurrent"]) // 2],
             "chunked_seqsplit_tokens_per_s": small_tokens / (avg["small_chunked_seqsplit"] / 1e3),
             "chunked_tokens_per_s": small_tokens / (avg["small_chunked"] / 1e3),
             "recurrent_tokens_per_s": small_tokens / (avg["small_recurrent"] / 1e3),
